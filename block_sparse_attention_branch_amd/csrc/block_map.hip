@@ -1,0 +1,278 @@
+// Inverted block map: for every (batch, group, KV block j) the queries t that
+// selected j (other than the queries of block j itself, whose "own block" is
+// always j), in increasing t.  This is the transpose of block_idx.
+//
+// Page: "How Flash-MSA cuts million-token training cost with sparse-k",
+// 'Kernel design and execution': the fused backward inverts the block-index
+// map so that query chunks can be scheduled around each sparse KV block;
+// "How to solve the memory problem with MiniMax Sparse Attention", 'Kernel
+// optimizations': the KV-outer kernels iterate over KV blocks rather than
+// queries.  Both kernels here consume this map.
+//
+// Layout (per (b, g) region, bg = b * H_kv + g):
+//   cnt/pos [nsb + 1][nblk]  pos[s][j] = entries of list j from query
+//            super-blocks < s (a super-block is SB query blocks); row nsb holds
+//            the list lengths.
+//   offs [nblk + 1]          start of list j inside the (b, g) entry region
+//   rows [N * topk]          entries (t << 6) | slot, slot = position of j in
+//                            block_idx[b, t, g, :] (at most topk - 1 per query
+//                            for a well-formed row; room for topk keeps a
+//                            malformed row in bounds)
+// Built by count -> column scan -> row scan -> ordered scatter.  Every step is
+// deterministic: the scatter walks each super-block's queries in order.
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+// Query blocks per super-block: the smallest power of two that keeps the
+// count matrix under 256 MiB.
+int super_block(const Problem& P) {
+  int sb = 1;
+  while (sb < 64) {
+    const size_t nsb = (size_t)(P.nblk + sb - 1) / sb;
+    const size_t bytes = (nsb + 1) * P.nblk * sizeof(int32_t) * P.B * P.H_kv;
+    if (bytes <= (size_t(256) << 20)) break;
+    sb *= 2;
+  }
+  return sb;
+}
+
+// Count the non-own selections of every KV block inside one super-block of
+// queries.  One workgroup per (b, g, super-block); counters in LDS.
+__global__ __launch_bounds__(256) void bm_count_kernel(const int32_t* __restrict__ block_idx,
+                                                       int32_t* __restrict__ pos, int N, int H_kv,
+                                                       int topk, int nblk, int nsb, int SB) {
+  extern __shared__ int32_t cnt[];
+  const int s = blockIdx.x % nsb;
+  const int bg = blockIdx.x / nsb;
+  const int b = bg / H_kv, g = bg % H_kv;
+  for (int j = threadIdx.x; j < nblk; j += blockDim.x) cnt[j] = 0;
+  __syncthreads();
+  const int t0 = s * SB * kBlock;
+  const int t1 = min(t0 + SB * kBlock, N);
+  const int n = (t1 - t0) * topk;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int t = t0 + i / topk, e = i % topk;
+    const int j = block_idx[(((size_t)b * N + t) * H_kv + g) * topk + e];
+    if ((unsigned)j < (unsigned)nblk && j != t / kBlock) atomicAdd(&cnt[j], 1);
+  }
+  __syncthreads();
+  int32_t* row = pos + ((size_t)bg * (nsb + 1) + s) * nblk;
+  for (int j = threadIdx.x; j < nblk; j += blockDim.x) row[j] = cnt[j];
+}
+
+// Exclusive scan of every column over super-blocks; row nsb gets the totals.
+__global__ __launch_bounds__(256) void bm_scan_cols_kernel(int32_t* __restrict__ pos, int nblk, int nsb,
+                                                           int n_bg) {
+  const int cols_per_bg = (nblk + 255) / 256;
+  const int bg = blockIdx.x / cols_per_bg;
+  const int j = (blockIdx.x % cols_per_bg) * 256 + threadIdx.x;
+  if (bg >= n_bg || j >= nblk) return;
+  int32_t* base = pos + (size_t)bg * (nsb + 1) * nblk + j;
+  int32_t run = 0;
+  for (int s = 0; s < nsb; ++s) {
+    const int32_t c = base[(size_t)s * nblk];
+    base[(size_t)s * nblk] = run;
+    run += c;
+  }
+  base[(size_t)nsb * nblk] = run;
+}
+
+// Block-wide exclusive scan of `in[0..n)` into `out[0..n]` (out[n] = total),
+// one workgroup of 1024 threads; each thread owns a contiguous run.
+__device__ void block_exclusive_scan(const int32_t* in, int32_t* out, int n, int stride_in) {
+  __shared__ int32_t part[1024];
+  const int T = blockDim.x;
+  const int per = (n + T - 1) / T;
+  const int lo = min(threadIdx.x * per, n), hi = min(lo + per, n);
+  int32_t sum = 0;
+  for (int i = lo; i < hi; ++i) sum += in[(size_t)i * stride_in];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the per-thread sums.
+  for (int off = 1; off < T; off <<= 1) {
+    const int32_t add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int32_t c = in[(size_t)i * stride_in];
+    out[i] = run;
+    run += c;
+  }
+  if (threadIdx.x == T - 1) out[n] = part[T - 1];
+}
+
+// offs[bg][j] = exclusive scan over j of the list lengths.
+__global__ __launch_bounds__(1024) void bm_offsets_kernel(const int32_t* __restrict__ pos,
+                                                          int32_t* __restrict__ offs, int nblk, int nsb) {
+  const int bg = blockIdx.x;
+  block_exclusive_scan(pos + ((size_t)bg * (nsb + 1) + nsb) * nblk, offs + (size_t)bg * (nblk + 1), nblk, 1);
+}
+
+// Ordered scatter: one wave per (b, g, super-block) walks its queries in
+// increasing t; lane e handles entry e of the query's row.  The entries of a
+// row name distinct blocks, so the LDS cursors never collide within a step.
+__global__ __launch_bounds__(64) void bm_scatter_kernel(const int32_t* __restrict__ block_idx,
+                                                        const int32_t* __restrict__ pos,
+                                                        const int32_t* __restrict__ offs,
+                                                        int32_t* __restrict__ rows, int N, int H_kv,
+                                                        int topk, int nblk, int nsb, int SB) {
+  extern __shared__ int32_t cursor[];
+  const int s = blockIdx.x % nsb;
+  const int bg = blockIdx.x / nsb;
+  const int b = bg / H_kv, g = bg % H_kv;
+  const int32_t* prow = pos + ((size_t)bg * (nsb + 1) + s) * nblk;
+  const int32_t* orow = offs + (size_t)bg * (nblk + 1);
+  for (int j = threadIdx.x; j < nblk; j += blockDim.x) cursor[j] = orow[j] + prow[j];
+  __syncthreads();
+  const int cap = N * topk;   // per (b, g): a row holds at most topk entries
+  int32_t* out = rows + (size_t)bg * cap;
+  const int t0 = s * SB * kBlock;
+  const int t1 = min(t0 + SB * kBlock, N);
+  const int e = threadIdx.x;
+  const bool active = e < topk;
+  const int32_t* src = block_idx + (((size_t)b * N) * H_kv + g) * topk + e;
+  const size_t tstride = (size_t)H_kv * topk;
+  int j_next = (active && t0 < t1) ? src[(size_t)t0 * tstride] : -1;
+  for (int t = t0; t < t1; ++t) {
+    const int j = j_next;
+    j_next = (active && t + 1 < t1) ? src[(size_t)(t + 1) * tstride] : -1;
+    if ((unsigned)j < (unsigned)nblk && j != t / kBlock) {
+      const int32_t p = cursor[j];
+      cursor[j] = p + 1;
+      if ((unsigned)p < (unsigned)cap) out[p] = (t << 6) | e;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int block_map_super_span(const Problem& P) { return super_block(P) * kBlock; }
+
+size_t block_map_bytes(const Problem& P) {
+  const int SB = super_block(P);
+  const size_t nsb = (size_t)(P.nblk + SB - 1) / SB;
+  const size_t bg = (size_t)P.B * P.H_kv;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  return al(bg * (nsb + 1) * P.nblk * 4) + al(bg * (P.nblk + 1) * 4) +
+         al(bg * (size_t)P.N * P.topk * 4) + al((bg * P.nblk + 1) * 4) + al(64 * 4);
+}
+
+void block_map_carve(const Problem& P, void* ws, BlockMap* m) {
+  const int SB = super_block(P);
+  const size_t nsb = (size_t)(P.nblk + SB - 1) / SB;
+  const size_t bg = (size_t)P.B * P.H_kv;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  char* p = static_cast<char*>(ws);
+  m->pos = reinterpret_cast<int32_t*>(p);
+  p += al(bg * (nsb + 1) * P.nblk * 4);
+  m->offs = reinterpret_cast<int32_t*>(p);
+  p += al(bg * (P.nblk + 1) * 4);
+  m->rows = reinterpret_cast<int32_t*>(p);
+  p += al(bg * (size_t)P.N * P.topk * 4);
+  m->tiles = reinterpret_cast<int32_t*>(p);
+  p += al((bg * P.nblk + 1) * 4);
+  m->counters = reinterpret_cast<int32_t*>(p);
+  m->SB = SB;
+  m->nsb = (int)nsb;
+}
+
+hipError_t launch_block_map(const Problem& P, const int32_t* block_idx, const BlockMap& m,
+                            int /*tile_rows*/, hipStream_t s) {
+  const int n_bg = P.B * P.H_kv;
+  const size_t lds = (size_t)P.nblk * sizeof(int32_t);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t e;
+  if (lds > 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bm_count_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bm_scatter_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bm_count_kernel, dim3(n_bg * m.nsb), dim3(256), lds, s, block_idx, m.pos, P.N,
+                     P.H_kv, P.topk, P.nblk, m.nsb, m.SB);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int cols_per_bg = (P.nblk + 255) / 256;
+  hipLaunchKernelGGL(bm_scan_cols_kernel, dim3(n_bg * cols_per_bg), dim3(256), 0, s, m.pos, P.nblk,
+                     m.nsb, n_bg);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bm_offsets_kernel, dim3(n_bg), dim3(1024), 0, s, m.pos, m.offs, P.nblk, m.nsb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (P.topk > 1) {
+    hipLaunchKernelGGL(bm_scatter_kernel, dim3(n_bg * m.nsb), dim3(64), lds, s, block_idx, m.pos, m.offs,
+                       m.rows, P.N, P.H_kv, P.topk, P.nblk, m.nsb, m.SB);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Work items of the KV-outer kernels for the query range [c0, c1): per list
+// (b, g, j) one diagonal item when block j lies in the range (its own 128
+// queries, causal mask) plus ceil(len / item_queries) items over the list
+// segment of the range.  tiles[] = exclusive scan over lists, tiles[n] = total.
+namespace {
+__global__ __launch_bounds__(1024) void bm_items_kernel(const int32_t* __restrict__ pos,
+                                                        int32_t* __restrict__ tiles, int nblk, int nsb,
+                                                        int n_bg, int s_lo, int s_hi, int jb_lo, int jb_hi,
+                                                        int item_queries) {
+  // Count items per list into tiles[], then scan in place (two passes over a
+  // small array; one workgroup).
+  const int n = n_bg * nblk;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int bg = i / nblk, j = i % nblk;
+    const int32_t* pb = pos + (size_t)bg * (nsb + 1) * nblk + j;
+    const int len = pb[(size_t)s_hi * nblk] - pb[(size_t)s_lo * nblk];
+    const int diag = (j >= jb_lo && j < jb_hi) ? 1 : 0;
+    tiles[i] = diag + (len + item_queries - 1) / item_queries;
+  }
+  __syncthreads();
+  // In-place exclusive scan with a one-workgroup pass over contiguous runs.
+  __shared__ int32_t part[1024];
+  const int T = blockDim.x;
+  const int per = (n + T - 1) / T;
+  const int lo = min((int)threadIdx.x * per, n), hi = min(lo + per, n);
+  int32_t sum = 0;
+  for (int i = lo; i < hi; ++i) sum += tiles[i];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int off = 1; off < T; off <<= 1) {
+    const int32_t add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int32_t c = tiles[i];
+    tiles[i] = run;
+    run += c;
+  }
+  if (threadIdx.x == T - 1) tiles[n] = part[T - 1];
+}
+}  // namespace
+
+hipError_t launch_block_items(const Problem& P, const BlockMap& m, int q_lo, int q_hi, int item_queries,
+                              hipStream_t s) {
+  const int n_bg = P.B * P.H_kv;
+  const int s_lo = q_lo / (m.SB * kBlock);
+  const int s_hi = (q_hi == P.N) ? m.nsb : q_hi / (m.SB * kBlock);
+  hipLaunchKernelGGL(bm_items_kernel, dim3(1), dim3(1024), 0, s, m.pos, m.tiles, P.nblk, m.nsb, n_bg, s_lo,
+                     s_hi, q_lo / kBlock, (q_hi + kBlock - 1) / kBlock, item_queries);
+  return hipGetLastError();
+}
+
+size_t block_items_upper_bound(const Problem& P, int q_lo, int q_hi, int item_queries) {
+  const size_t n_bg = (size_t)P.B * P.H_kv;
+  const size_t diag = (size_t)(q_hi - q_lo + kBlock - 1) / kBlock;
+  const size_t entries = (size_t)(q_hi - q_lo) * P.topk;
+  return n_bg * (diag + P.nblk + entries / item_queries + 1);
+}
+
+}  // namespace msa

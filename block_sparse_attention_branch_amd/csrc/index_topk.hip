@@ -1,0 +1,258 @@
+// Index branch of MiniMax Sparse Attention, fused in one pass: index scores
+// (MFMA), block max-pool (in registers) and the exp-free top-k with the
+// query's own block forced (a per-lane sorted list in registers).
+//
+// Pages: "How to solve the memory problem with MiniMax Sparse Attention",
+// 'How the indexer works' (score visible tokens with the group's index query
+// against the shared index key, max-pool per block, keep the top k with the
+// own block always in) and 'Kernel optimizations' (softmax keeps the order,
+// so the top-k skips exp and sum); "How Flash-MSA cuts million-token training
+// cost with sparse-k", 'Block sparsity mechanism' and 'Kernel design and
+// execution' (the proxy pass accumulates no output, only scores and top-k
+// indices, kept in registers).
+//
+// Work split.  A workgroup of 8 waves streams the index keys of one batch
+// row block by block (128 keys per block, staged in LDS, double buffered).
+// Each wave owns 64 queries of one group.  For a block it computes the
+// 128 x 64 score tile as S^T = K_idx Q_idx^T with 32x32 MFMA tiles: keys are
+// the tile rows, queries the columns, so a lane holds one query and 16 keys
+// per tile and the block max is a register max plus one exchange between the
+// two half-waves.  After the exchange lane l owns query q0 + l and folds the
+// block's pooled score into its sorted list of the best topk-1 other blocks
+// (strictly greater wins, so equal scores keep the lower block index).  No
+// pooled score ever reaches HBM unless the caller asks for it.
+#include <float.h>
+#include <limits.h>
+
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+constexpr int kIdxWaves = 8;
+constexpr int kIdxThreads = kIdxWaves * kWave;
+constexpr int kQPerWave = 64;
+
+template <typename T, int DIDX>
+struct IdxCfg {
+  static constexpr int KPL = Mma<T>::KPL;
+  static constexpr int KSTEPS = DIDX / (2 * KPL);
+  static constexpr int PITCH = DIDX + 16 / (int)sizeof(T);    // LDS row, 16 B pad
+  static constexpr int TILE_ELEMS = kBlock * PITCH;
+  static constexpr int CHUNKS_PER_ROW = DIDX * (int)sizeof(T) / 16;
+  static constexpr int CHUNKS_PER_THREAD = kBlock * CHUNKS_PER_ROW / kIdxThreads;
+  static_assert(kBlock * CHUNKS_PER_ROW % kIdxThreads == 0, "tile load must split evenly");
+  static constexpr size_t LDS_BYTES = 2 * TILE_ELEMS * sizeof(T);
+};
+
+template <typename T, int DIDX, int CAP>
+__global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
+    const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
+    float* __restrict__ pooled, int N, int H_kv, int topk, int causal, int GT, int n_qtiles,
+    int n_gtiles) {
+  using C = IdxCfg<T, DIDX>;
+  using M = Mma<T>;
+  constexpr int KPL = C::KPL;
+  extern __shared__ __align__(16) char smem_raw[];
+  T* lds = reinterpret_cast<T*>(smem_raw);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int QW = kIdxWaves / GT;
+  const int nblk = N / kBlock;
+
+  // Heaviest (latest) query tiles first: causal work grows with the tile.
+  const int per_q = gridDim.x / n_qtiles;
+  const int qrev = blockIdx.x / per_q;
+  const int rest = blockIdx.x % per_q;
+  const int b = rest / n_gtiles;
+  const int gtile = rest % n_gtiles;
+  const int qtile = n_qtiles - 1 - qrev;
+  const int g = gtile * GT + (wave % GT);
+  const int wg_q0 = qtile * QW * kQPerWave;
+  const int q0 = wg_q0 + (wave / GT) * kQPerWave;
+  const bool wave_valid = q0 < N;
+  const int own = (wave_valid ? q0 : N - 1) / kBlock;   // shared by the wave's 64 queries
+  const int wg_last = min(wg_q0 + QW * kQPerWave - 1, N - 1);
+  const int jlast = causal ? wg_last / kBlock : nblk - 1;
+
+  // Index-query fragments (B operand) for the wave's two 32-query columns.
+  typename M::frag qf[2][C::KSTEPS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int t = min(q0 + nt * 32 + (lane & 31), N - 1);
+    const T* qp = q_idx + (((size_t)b * N + t) * H_kv + g) * DIDX + KPL * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[nt][ks] = M::load(qp + ks * 2 * KPL);
+  }
+
+  float tv[CAP];
+  int ti[CAP];
+#pragma unroll
+  for (int i = 0; i < CAP; ++i) {
+    tv[i] = -INFINITY;
+    ti[i] = -1;
+  }
+
+  const char* kbase = reinterpret_cast<const char*>(k_idx + (size_t)b * N * DIDX);
+  uint4 stage[C::CHUNKS_PER_THREAD];
+  auto load_block = [&](int j) {
+    const char* src = kbase + (size_t)j * kBlock * DIDX * sizeof(T);
+#pragma unroll
+    for (int c = 0; c < C::CHUNKS_PER_THREAD; ++c) {
+      const int chunk = threadIdx.x + c * kIdxThreads;
+      stage[c] = *reinterpret_cast<const uint4*>(src + (size_t)chunk * 16);
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < C::CHUNKS_PER_THREAD; ++c) {
+      const int chunk = threadIdx.x + c * kIdxThreads;
+      const int row = chunk / C::CHUNKS_PER_ROW, col = chunk % C::CHUNKS_PER_ROW;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds + buf * C::TILE_ELEMS + row * C::PITCH) +
+                                col * 16) = stage[c];
+    }
+  };
+
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+
+  for (int j = 0; j <= jlast; ++j) {
+    const int buf = j & 1;
+    const bool more = j < jlast;
+    if (more) load_block(j + 1);
+    const bool visible = wave_valid && (!causal || j <= own);
+    const bool is_own = j == own;
+    if (visible && (!is_own || pooled != nullptr)) {
+      float run0 = -INFINITY, run1 = -INFINITY;
+      const T* tile = lds + buf * C::TILE_ELEMS;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x16 a0 = zero16(), a1 = zero16();
+        const T* ap = tile + (mt * 32 + (lane & 31)) * C::PITCH + KPL * (lane >> 5);
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+          const typename M::frag a = M::load(ap + ks * 2 * KPL);
+          a0 = M::mma(a, qf[0][ks], a0);
+          a1 = M::mma(a, qf[1][ks], a1);
+        }
+        if (is_own && causal) {
+          // Diagonal block: only keys u <= t are visible to query t.
+          const int t0 = q0 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int u = j * kBlock + mt * 32 + c_row(v, lane);
+            if (u > t0) a0[v] = -INFINITY;
+            if (u > t0 + 32) a1[v] = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          run0 = fmaxf(run0, a0[v]);
+          run1 = fmaxf(run1, a1[v]);
+        }
+      }
+      // Lanes l and l^32 hold the two key halves of the same query column.
+      const float recv = swap_half(lane < 32 ? run1 : run0);
+      const float p = fmaxf(lane < 32 ? run0 : run1, recv);   // pooled score of query q0+lane
+      const int tq = q0 + lane;
+      if (pooled != nullptr && tq < N) pooled[(((size_t)b * N + tq) * H_kv + g) * nblk + j] = p;
+      if (!is_own) {
+#pragma unroll
+        for (int i = CAP - 1; i >= 1; --i) {
+          const bool up = p > tv[i - 1];
+          const bool here = p > tv[i];
+          tv[i] = up ? tv[i - 1] : (here ? p : tv[i]);
+          ti[i] = up ? ti[i - 1] : (here ? j : ti[i]);
+        }
+        const bool here = p > tv[0];
+        tv[0] = here ? p : tv[0];
+        ti[0] = here ? j : ti[0];
+      }
+    }
+    if (more) store_block(buf ^ 1);
+    __syncthreads();
+  }
+
+  const int tq = q0 + lane;
+  if (!wave_valid || tq >= N) return;
+  // Own block plus the first topk-1 list entries, written in ascending order.
+  int E[CAP + 1];
+  E[0] = own;
+#pragma unroll
+  for (int i = 0; i < CAP; ++i) E[i + 1] = (i < topk - 1) ? ti[i] : -1;
+  int32_t* out = block_idx + (((size_t)b * N + tq) * H_kv + g) * topk;
+#pragma unroll
+  for (int i = 0; i <= CAP; ++i) {
+    const int ki = E[i] < 0 ? INT_MAX : E[i];
+    int rank = 0;
+#pragma unroll
+    for (int k = 0; k <= CAP; ++k) {
+      const int kk = E[k] < 0 ? INT_MAX : E[k];
+      rank += (kk < ki) || (kk == ki && k < i);
+    }
+    if (rank < topk) out[rank] = E[i];
+  }
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, size_t n, float value) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+template <typename T, int DIDX, int CAP>
+hipError_t launch_typed(const Problem& P, const void* q_idx, const void* k_idx, int32_t* block_idx,
+                        float* pooled, hipStream_t s) {
+  using C = IdxCfg<T, DIDX>;
+  int GT = 1;
+  while (GT < kIdxWaves && P.H_kv % (GT * 2) == 0) GT *= 2;
+  const int QW = kIdxWaves / GT;
+  const int n_qtiles = (P.N + QW * kQPerWave - 1) / (QW * kQPerWave);
+  const int n_gtiles = P.H_kv / GT;
+  const dim3 grid(n_qtiles * P.B * n_gtiles);
+  auto kern = index_topk_kernel<T, DIDX, CAP>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(kIdxThreads), C::LDS_BYTES, s, static_cast<const T*>(q_idx),
+                     static_cast<const T*>(k_idx), block_idx, pooled, P.N, P.H_kv, P.topk, P.causal,
+                     GT, n_qtiles, n_gtiles);
+  return hipGetLastError();
+}
+
+template <typename T, int DIDX>
+hipError_t launch_cap(const Problem& P, const void* q, const void* k, int32_t* bi, float* pooled,
+                      hipStream_t s) {
+  const int need = P.topk - 1;
+  if (need <= 3) return launch_typed<T, DIDX, 3>(P, q, k, bi, pooled, s);
+  if (need <= 7) return launch_typed<T, DIDX, 7>(P, q, k, bi, pooled, s);
+  if (need <= 15) return launch_typed<T, DIDX, 15>(P, q, k, bi, pooled, s);
+  return launch_typed<T, DIDX, 31>(P, q, k, bi, pooled, s);
+}
+
+}  // namespace
+
+hipError_t launch_fill_f32(float* p, size_t n, float value, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t want = (n + 255) / 256;
+  const int blocks = (int)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const Problem& P, const void* q_idx, const void* k_idx,
+                             int32_t* block_idx, float* pooled, hipStream_t s) {
+  if (pooled != nullptr) {
+    hipError_t e = launch_fill_f32(pooled, (size_t)P.B * P.N * P.H_kv * P.nblk, -INFINITY, s);
+    if (e != hipSuccess) return e;
+  }
+  if (P.dtype == MSA_BF16) {
+    if (P.d_idx == 64) return launch_cap<bf16, 64>(P, q_idx, k_idx, block_idx, pooled, s);
+    return launch_cap<bf16, 32>(P, q_idx, k_idx, block_idx, pooled, s);
+  }
+  if (P.d_idx == 64) return launch_cap<float, 64>(P, q_idx, k_idx, block_idx, pooled, s);
+  return launch_cap<float, 32>(P, q_idx, k_idx, block_idx, pooled, s);
+}
+
+}  // namespace msa

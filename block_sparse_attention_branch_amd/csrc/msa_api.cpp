@@ -1,0 +1,222 @@
+// C-ABI entry points of libmsa: argument validation, workspace planning and
+// kernel dispatch on the caller's stream.  The interface and its conventions
+// are documented in include/msa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "msa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MSA_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Largest sequence length the block map's entry encoding (t << 6 | slot)
+// can hold in an int32.
+constexpr int kMaxN = 1 << 22;
+
+int check_dims(const msa_dims* d, msa::Problem* P) {
+  if (d == nullptr) return fail(MSA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->B <= 0 || d->N <= 0 || d->H_q <= 0 || d->H_kv <= 0 || d->d <= 0 || d->d_idx <= 0 ||
+      d->block_size <= 0 || d->topk <= 0)
+    return fail(MSA_ERR_INVALID_ARG,
+                "dimensions must be positive (B=%d N=%d H_q=%d H_kv=%d d=%d d_idx=%d block_size=%d topk=%d)",
+                d->B, d->N, d->H_q, d->H_kv, d->d, d->d_idx, d->block_size, d->topk);
+  if (d->H_q % d->H_kv != 0)
+    return fail(MSA_ERR_INVALID_ARG, "H_q=%d is not a multiple of H_kv=%d", d->H_q, d->H_kv);
+  if (d->causal != 0 && d->causal != 1) return fail(MSA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (d->dtype != MSA_F32 && d->dtype != MSA_BF16)
+    return fail(MSA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (!std::isfinite(d->scale) || d->scale < 0.f || !std::isfinite(d->scale_idx) || d->scale_idx < 0.f)
+    return fail(MSA_ERR_INVALID_ARG, "scale and scale_idx must be finite and >= 0");
+  if (d->block_size != msa::kBlock)
+    return fail(MSA_ERR_UNSUPPORTED, "block_size=%d (only %d is built)", d->block_size, msa::kBlock);
+  if (d->N % msa::kBlock != 0)
+    return fail(MSA_ERR_UNSUPPORTED, "N=%d is not a multiple of the block size %d", d->N, msa::kBlock);
+  if (d->N > kMaxN) return fail(MSA_ERR_UNSUPPORTED, "N=%d exceeds %d", d->N, kMaxN);
+  if (d->d != 64 && d->d != 128) return fail(MSA_ERR_UNSUPPORTED, "head dim d=%d (64 or 128)", d->d);
+  if (d->d_idx != 32 && d->d_idx != 64)
+    return fail(MSA_ERR_UNSUPPORTED, "index dim d_idx=%d (32 or 64)", d->d_idx);
+  if (d->topk > 32) return fail(MSA_ERR_UNSUPPORTED, "topk=%d (at most 32)", d->topk);
+  const int G = d->H_q / d->H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(MSA_ERR_UNSUPPORTED, "group size H_q/H_kv=%d (1, 2, 4, 8 or 16)", G);
+  P->B = d->B;
+  P->N = d->N;
+  P->H_q = d->H_q;
+  P->H_kv = d->H_kv;
+  P->G = G;
+  P->d = d->d;
+  P->d_idx = d->d_idx;
+  P->topk = d->topk;
+  P->causal = d->causal;
+  P->dtype = d->dtype;
+  P->nblk = d->N / msa::kBlock;
+  P->scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->d);
+  P->scale_idx = d->scale_idx > 0.f ? d->scale_idx : 1.0f / std::sqrt((float)d->d_idx);
+  return MSA_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (have < need) return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", have, need);
+  if (need > 0 && ws == nullptr) return fail(MSA_ERR_INVALID_ARG, "workspace is NULL");
+  return MSA_OK;
+}
+
+#define REQUIRE(ptr)                                                                       \
+  do {                                                                                     \
+    if ((ptr) == nullptr) return fail(MSA_ERR_INVALID_ARG, "required pointer %s is NULL", #ptr); \
+  } while (0)
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Queries per forward launch: bounds the partial-result buffer (one output
+// row in the dtype plus one fp32 log-sum-exp per (batch, query, head, slot))
+// to ~8 GiB.  A multiple of the block map's super-block span.
+int fwd_chunk_queries(const msa::Problem& P) {
+  const size_t esz = P.dtype == MSA_BF16 ? 2 : 4;
+  const size_t per_query = (size_t)P.B * P.H_q * P.topk * (P.d * esz + sizeof(float));
+  const size_t cap = size_t(8) << 30;
+  const size_t span = (size_t)msa::block_map_super_span(P);
+  size_t q = cap / per_query;
+  q -= q % span;
+  if (q < span) q = span;
+  if (q >= (size_t)P.N) q = P.N;
+  return (int)q;
+}
+
+}  // namespace
+
+extern "C" {
+
+MSA_API int msa_version(void) { return 1; }
+
+MSA_API const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARG: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported problem";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+MSA_API const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+MSA_API size_t msa_index_topk_workspace(const msa_dims* dims) {
+  msa::Problem P;
+  if (check_dims(dims, &P) != MSA_OK) return 0;
+  return 0;
+}
+
+MSA_API int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx,
+                           int32_t* block_idx, float* pooled, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  msa::Problem P;
+  int st = check_dims(dims, &P);
+  if (st != MSA_OK) return st;
+  REQUIRE(q_idx);
+  REQUIRE(k_idx);
+  REQUIRE(block_idx);
+  st = check_ws(workspace, workspace_bytes, 0);
+  if (st != MSA_OK) return st;
+  hipError_t e = msa::launch_index_topk(P, q_idx, k_idx, block_idx, pooled, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "msa_index_topk launch");
+  return ok();
+}
+
+MSA_API size_t msa_sparse_fwd_workspace(const msa_dims* dims) {
+  msa::Problem P;
+  if (check_dims(dims, &P) != MSA_OK) return 0;
+  return align_up(msa::block_map_bytes(P)) + align_up(msa::sparse_fwd_partials_bytes(P, fwd_chunk_queries(P)));
+}
+
+MSA_API int msa_sparse_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
+                           const int32_t* block_idx, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  msa::Problem P;
+  int st = check_dims(dims, &P);
+  if (st != MSA_OK) return st;
+  REQUIRE(q);
+  REQUIRE(k);
+  REQUIRE(v);
+  REQUIRE(block_idx);
+  REQUIRE(o);
+  REQUIRE(lse);
+  const int chunk = fwd_chunk_queries(P);
+  const size_t map_bytes = align_up(msa::block_map_bytes(P));
+  st = check_ws(workspace, workspace_bytes, map_bytes + align_up(msa::sparse_fwd_partials_bytes(P, chunk)));
+  if (st != MSA_OK) return st;
+  msa::BlockMap m;
+  msa::block_map_carve(P, workspace, &m);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = msa::launch_block_map(P, block_idx, m, 0, s);
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_fwd block map");
+  e = msa::launch_sparse_fwd(P, q, k, v, block_idx, o, lse, m, static_cast<char*>(workspace) + map_bytes,
+                             chunk, s);
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_fwd launch");
+  return ok();
+}
+
+MSA_API size_t msa_sparse_bwd_workspace(const msa_dims* dims) {
+  msa::Problem P;
+  if (check_dims(dims, &P) != MSA_OK) return 0;
+  return 0;
+}
+
+MSA_API int msa_sparse_bwd(const msa_dims* dims, const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           const int32_t* block_idx, const void* q_idx, const void* k_idx,
+                           float kl_weight, void* dq, void* dk, void* dv, float* dq_idx,
+                           float* dk_idx, float* dscore, float* kl, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  msa::Problem P;
+  int st = check_dims(dims, &P);
+  if (st != MSA_OK) return st;
+  REQUIRE(q);
+  REQUIRE(k);
+  REQUIRE(v);
+  REQUIRE(o);
+  REQUIRE(dO);
+  REQUIRE(lse);
+  REQUIRE(block_idx);
+  REQUIRE(q_idx);
+  REQUIRE(k_idx);
+  REQUIRE(dq);
+  REQUIRE(dk);
+  REQUIRE(dv);
+  REQUIRE(dq_idx);
+  REQUIRE(dk_idx);
+  if (!std::isfinite(kl_weight)) return fail(MSA_ERR_INVALID_ARG, "kl_weight must be finite");
+  (void)dscore;
+  (void)kl;
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)stream;
+  return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_bwd is not built yet");
+}
+
+}  // extern "C"

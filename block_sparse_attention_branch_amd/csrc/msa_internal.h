@@ -1,0 +1,112 @@
+// Internal declarations and device helpers shared by the libmsa kernels.
+// Not part of the public interface (include/msa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/msa.h"
+
+namespace msa {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kBlock = 128;     // KV block size the kernels are built for
+constexpr int kWave = 64;       // CDNA wavefront width
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.  A 32x32 output tile D[m][n] lives in 16 fp32 slots per
+// lane: lane l holds column n = l % 32 and rows m = 8*(v/4) + 4*(l/32) + v%4
+// for slot v (checked on gfx950 hardware).  A-operand lane l holds row
+// m = l % 32, B-operand lane l holds column n = l % 32; both hold the same
+// KPL consecutive k values, k = KPL*(l/32) + i, of the instruction's 2*KPL.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+  typedef bf16x8 frag;
+  static constexpr int KPL = 8;   // k values per lane per instruction
+  __device__ static inline frag load(const bf16* p) {
+    return *reinterpret_cast<const frag*>(p);
+  }
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  typedef float frag;
+  static constexpr int KPL = 1;
+  __device__ static inline frag load(const float* p) { return *p; }
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Row index inside a 32x32 tile held by slot v of lane l.
+__device__ inline int c_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Exchange a value with the lane 32 places away (lane l <-> l ^ 32).
+__device__ inline float swap_half(float x) { return __shfl_xor(x, 32); }
+__device__ inline int swap_half(int x) { return __shfl_xor(x, 32); }
+
+// ---------------------------------------------------------------------------
+// Launchers (one per kernel family); each returns hipGetLastError().
+// ---------------------------------------------------------------------------
+struct Problem {
+  int B, N, H_q, H_kv, G, d, d_idx, topk, causal, dtype, nblk;
+  float scale, scale_idx;
+};
+
+hipError_t launch_fill_f32(float* p, size_t n, float value, hipStream_t s);
+
+hipError_t launch_index_topk(const Problem& P, const void* q_idx, const void* k_idx,
+                             int32_t* block_idx, float* pooled, hipStream_t s);
+
+// Inverted block map (CSR of the queries that selected each KV block).
+struct BlockMap {
+  int32_t* pos;      // [B*H_kv][nsb + 1][nblk]: entries of list j from super-blocks < s
+  int32_t* offs;     // [B*H_kv][nblk + 1]: start of list j in the (b, g) entry region
+  int32_t* rows;     // [B*H_kv][N * topk]: entries (t << 6) | slot, t-sorted per list
+  int32_t* tiles;    // [B*H_kv*nblk + 1]: exclusive scan of work items per list
+  int32_t* counters; // small scratch
+  int SB;            // query blocks per super-block
+  int nsb;           // super-blocks
+};
+size_t block_map_bytes(const Problem& P);
+void block_map_carve(const Problem& P, void* ws, BlockMap* m);
+hipError_t launch_block_map(const Problem& P, const int32_t* block_idx, const BlockMap& m,
+                            int tile_rows, hipStream_t s);
+// Work items of the KV-outer kernels for queries [q_lo, q_hi) (q_lo a
+// multiple of the super-block span).
+hipError_t launch_block_items(const Problem& P, const BlockMap& m, int q_lo, int q_hi,
+                              int item_queries, hipStream_t s);
+size_t block_items_upper_bound(const Problem& P, int q_lo, int q_hi, int item_queries);
+int block_map_super_span(const Problem& P);  // queries per super-block
+
+size_t sparse_fwd_partials_bytes(const Problem& P, int chunk_queries);
+hipError_t launch_sparse_fwd(const Problem& P, const void* q, const void* k, const void* v,
+                             const int32_t* block_idx, void* o, float* lse, const BlockMap& m,
+                             void* partials, int chunk_queries, hipStream_t s);
+
+}  // namespace msa

@@ -150,12 +150,15 @@ def index_topk(q_idx: np.ndarray, k_idx: np.ndarray, block_size: int, topk: int,
     asked, pooled scores of the same leading shape with nblk columns."""
     q_idx = np.asarray(q_idx)
     k_idx = np.asarray(k_idx)
-    B, N, H_kv, _ = q_idx.shape
+    B, N, d_idx = k_idx.shape
+    H_kv = q_idx.shape[-2]
     nb = n_blocks(N, block_size)
     if rows is None:
         bt = [(b, t) for b in range(B) for t in range(N)]
     else:
         bt = [(int(b), int(t)) for b, t in rows]
+    # With `rows`, q_idx may be compact: [len(rows), H_kv, d_idx].
+    compact = rows is not None and q_idx.ndim == 3
     out = np.full((len(bt), H_kv, topk), -1, dtype=np.int64)
     pooled_out = np.full((len(bt), H_kv, nb), NEG_INF) if want_pooled else None
     for b in sorted({b for b, _ in bt}):
@@ -164,7 +167,8 @@ def index_topk(q_idx: np.ndarray, k_idx: np.ndarray, block_size: int, topk: int,
             ii = idx[c0:c0 + chunk]
             ts = np.array([bt[i][1] for i in ii])
             for g in range(H_kv):
-                r = index_scores_rows(q_idx[b, ts, g, :], k_idx[b], ts, causal)
+                qrows = q_idx[ii, g, :] if compact else q_idx[b, ts, g, :]
+                r = index_scores_rows(qrows, k_idx[b], ts, causal)
                 pooled = block_maxpool_rows(r, block_size)
                 for m, i in enumerate(ii):
                     out[i, g] = select_blocks_row(pooled[m], int(ts[m]), block_size, topk, causal)
@@ -206,22 +210,26 @@ def sparse_fwd(q, k, v, block_idx, block_size: int, causal: bool = True,
     ([MSA] "Two-stage process": selection is joint for a group's queries).
 
     Returns O [B,N,H_q,d] and LSE [B,N,H_q] (or [len(rows), ...])."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    # Arrays keep their (exact) input precision; gathered rows are upcast to
+    # fp64 where they are used.  With `rows`, q may be compact
+    # [len(rows), H_q, d].
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     block_idx = np.asarray(block_idx)
-    B, N, H_q, d = q.shape
-    H_kv = k.shape[2]
+    B, N, H_kv, d = k.shape
+    H_q = q.shape[-2]
     G = H_q // H_kv
     scale = default_scale(d) if scale is None else scale
     bt = [(b, t) for b in range(B) for t in range(N)] if rows is None else [(int(b), int(t)) for b, t in rows]
+    compact = rows is not None and q.ndim == 3
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
     O = np.zeros((len(bt), H_q, v.shape[3]))
     L = np.zeros((len(bt), H_q))
     for i, (b, t) in enumerate(bt):
+        qrow = q[i] if compact else q[b, t]
         for g in range(H_kv):
             S = support(block_idx[b, t, g], t, N, block_size, causal)
             hs = slice(g * G, (g + 1) * G)
-            o, lse, _ = _attend(q[b, t, hs], k[b, S, g], v[b, S, g], scale)
+            o, lse, _ = _attend(f64(qrow[hs]), f64(k[b, S, g]), f64(v[b, S, g]), scale)
             O[i, hs] = o
             L[i, hs] = lse
     if rows is None:
@@ -298,35 +306,38 @@ def sparse_bwd(q, k, v, dO, q_idx, k_idx, block_idx, block_size: int,
     zero at masked or padded positions.  With `rows`, only those (b, t) rows
     contribute (dq/dq_idx/kl/dscore are returned for those rows only; dk, dv,
     dk_idx hold those rows' contributions)."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    dO = np.asarray(dO, dtype=np.float64)
-    q_idx = np.asarray(q_idx, dtype=np.float64)
-    k_idx = np.asarray(k_idx, dtype=np.float64)
+    # Per-row fp64 upcast as in sparse_fwd; with `rows`, q, dO and q_idx may
+    # be compact ([len(rows), ...]).  dk, dv, dk_idx are full-size fp64.
+    q, k, v, dO = np.asarray(q), np.asarray(k), np.asarray(v), np.asarray(dO)
+    q_idx, k_idx = np.asarray(q_idx), np.asarray(k_idx)
     block_idx = np.asarray(block_idx)
-    B, N, H_q, d = q.shape
-    H_kv = k.shape[2]
+    B, N, H_kv, d = k.shape
+    H_q = q.shape[-2]
     G = H_q // H_kv
     topk = block_idx.shape[3]
-    d_idx = q_idx.shape[3]
+    d_idx = k_idx.shape[2]
     scale = default_scale(d) if scale is None else scale
     scale_idx = default_scale(d_idx) if scale_idx is None else scale_idx
     bt = [(b, t) for b in range(B) for t in range(N)] if rows is None else [(int(b), int(t)) for b, t in rows]
+    compact = rows is not None and q.ndim == 3
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
     R = len(bt)
     dq = np.zeros((R, H_q, d))
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
     dq_idx = np.zeros((R, H_kv, d_idx))
-    dk_idx = np.zeros_like(k_idx)
+    dk_idx = np.zeros(k_idx.shape)
     kl = np.zeros((R, H_kv))
     dscore = np.zeros((R, H_kv, topk, block_size)) if want_dscore else None
     for i, (b, t) in enumerate(bt):
+        qrow = q[i] if compact else q[b, t]
+        dorow = dO[i] if compact else dO[b, t]
+        qirow = q_idx[i] if compact else q_idx[b, t]
         for g in range(H_kv):
             S = support(block_idx[b, t, g], t, N, block_size, causal)
             hs = slice(g * G, (g + 1) * G)
-            Qg, dOg = q[b, t, hs], dO[b, t, hs]
-            KS, VS = k[b, S, g], v[b, S, g]
+            Qg, dOg = f64(qrow[hs]), f64(dorow[hs])
+            KS, VS = f64(k[b, S, g]), f64(v[b, S, g])
             _, _, P = _attend(Qg, KS, VS, scale)          # [G, |S|]
             dP = dOg @ VS.T
             dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
@@ -336,12 +347,13 @@ def sparse_bwd(q, k, v, dO, q_idx, k_idx, block_idx, block_size: int,
             dv[b, S, g] += P.T @ dOg
             # KL-alignment on the same support.
             pbar = P.mean(axis=0)
-            z = scale_idx * (k_idx[b, S] @ q_idx[b, t, g])
+            qi_g, kS_idx = f64(qirow[g]), f64(k_idx[b, S])
+            z = scale_idx * (kS_idx @ qi_g)
             z = z - z.max()
             p_px = np.exp(z) / np.exp(z).sum()
             dz = kl_weight * (p_px - pbar)
-            dq_idx[i, g] = scale_idx * dz @ k_idx[b, S]
-            dk_idx[b, S] += scale_idx * np.outer(dz, q_idx[b, t, g])
+            dq_idx[i, g] = scale_idx * dz @ kS_idx
+            dk_idx[b, S] += scale_idx * np.outer(dz, qi_g)
             nz = pbar > 0
             kl[i, g] = float(np.sum(pbar[nz] * (np.log(pbar[nz]) - np.log(p_px[nz]))))
             if want_dscore:

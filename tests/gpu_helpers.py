@@ -1,0 +1,107 @@
+"""Shared helpers of the GPU parity tests: device gate, metrics, near-tie
+analysis of block selections and row sampling.  Imported by the gpu tests
+only (not collected by pytest itself)."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import msa_inputs
+from oracle import msa_oracle as O
+
+U32 = 2.0 ** -24
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import block_sparse_attention_branch_amd as msa
+    msa.load_library()          # loud failure if the library is missing
+    return msa
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def cosine(a, b):
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    return float(a @ b / math.sqrt((a @ a) * (b @ b)))
+
+
+def max_rel(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
+def f32(t: torch.Tensor):
+    """Exact host copy (bf16 and fp32 both fit in fp32)."""
+    return t.detach().float().cpu().numpy()
+
+
+def gamma(n: int) -> float:
+    return n * U32 / (1 - n * U32)
+
+
+def selection_equivalent(gpu_sel, ref_sel, ref_pooled_row, t, block_size, tol):
+    """True when the GPU's selection equals the oracle's, or differs only by
+    swapping blocks whose oracle pooled scores lie within `tol` of each
+    other (a near tie under fp32 accumulation).  Also checks validity: own
+    block present, ascending, distinct, -1 padding at the end."""
+    g = [int(x) for x in gpu_sel]
+    r = [int(x) for x in ref_sel]
+    if g == r:
+        return True
+    valid = [x for x in g if x >= 0]
+    if valid != sorted(set(valid)) or g[len(valid):] != [-1] * (len(g) - len(valid)):
+        return False
+    own = t // block_size
+    if own not in valid or len(valid) != len([x for x in r if x >= 0]):
+        return False
+    gv = sorted((ref_pooled_row[j] for j in valid if j != own), reverse=True)
+    rv = sorted((ref_pooled_row[j] for j in r if j >= 0 and j != own), reverse=True)
+    return all(abs(a - b) <= tol for a, b in zip(gv, rv))
+
+
+def row_tolerance(q_idx_row, k_idx_b, t, causal, d_idx):
+    """2 * gamma_{d_idx} * max_u sum_i |q_i k_i|: how far an fp32-accumulated
+    index score may sit from the exact one (Higham's bound), doubled for the
+    two scores compared."""
+    a = np.abs(np.asarray(q_idx_row, dtype=np.float64))
+    kk = np.abs(np.asarray(k_idx_b[: t + 1] if causal else k_idx_b, dtype=np.float64))
+    return 2.0 * gamma(d_idx) * float((kk @ a).max())
+
+
+def sample_rows(B, N, n, seed, extra=()):
+    """Seeded, stratified (b, t) rows: the edges of the selection budget plus
+    `extra` positions plus uniform picks."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 127, 128, 1919, 1920, 2047, 2048, N // 2, N - 129, N - 128, N - 1] + list(extra)
+    fixed = sorted({t for t in fixed if 0 <= t < N})
+    rows = [(b, t) for b in range(B) for t in fixed]
+    while len(rows) < n * B:
+        rows.append((int(rng.integers(B)), int(rng.integers(N))))
+    return sorted(set(rows))
+
+
+def fwd_chunk_queries(w: msa_inputs.Workload) -> int:
+    """Queries per forward launch, as the library plans it (for sampling rows
+    at chunk seams)."""
+    esz = 2 if w.dtype == "bf16" else 4
+    per_q = w.B * w.H_q * w.topk * (w.d * esz + 4)
+    nblk = w.N // w.block_size
+    sb = 1
+    while sb < 64 and ((nblk + sb - 1) // sb + 1) * nblk * 4 * w.B * w.H_kv > (256 << 20):
+        sb *= 2
+    span = sb * w.block_size
+    q = (8 << 30) // per_q
+    q -= q % span
+    return max(span, min(q, w.N))
