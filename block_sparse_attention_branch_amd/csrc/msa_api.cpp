@@ -184,7 +184,8 @@ MSA_API int msa_sparse_fwd(const msa_dims* dims, const void* q, const void* k, c
 MSA_API size_t msa_sparse_bwd_workspace(const msa_dims* dims) {
   msa::Problem P;
   if (check_dims(dims, &P) != MSA_OK) return 0;
-  return 0;
+  if (P.dtype != MSA_BF16) return 0;
+  return align_up(msa::block_map_bytes(P)) + align_up(msa::sparse_bwd_scratch_bytes(P));
 }
 
 MSA_API int msa_sparse_bwd(const msa_dims* dims, const void* q, const void* k, const void* v,
@@ -211,12 +212,21 @@ MSA_API int msa_sparse_bwd(const msa_dims* dims, const void* q, const void* k, c
   REQUIRE(dq_idx);
   REQUIRE(dk_idx);
   if (!std::isfinite(kl_weight)) return fail(MSA_ERR_INVALID_ARG, "kl_weight must be finite");
-  (void)dscore;
-  (void)kl;
-  (void)workspace;
-  (void)workspace_bytes;
-  (void)stream;
-  return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_bwd is not built yet");
+  if (P.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_bwd supports bf16 only");
+  const size_t map_bytes = align_up(msa::block_map_bytes(P));
+  st = check_ws(workspace, workspace_bytes, map_bytes + align_up(msa::sparse_bwd_scratch_bytes(P)));
+  if (st != MSA_OK) return st;
+  msa::BlockMap m;
+  msa::block_map_carve(P, workspace, &m);
+  msa::BwdScratch w;
+  msa::sparse_bwd_scratch_carve(P, static_cast<char*>(workspace) + map_bytes, &w);
+  msa::BwdArgs a{q, k, v, o, dO, lse, block_idx, q_idx, k_idx, kl_weight, dq, dk, dv, dq_idx, dk_idx, dscore, kl};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = msa::launch_block_map(P, block_idx, m, 0, s);
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_bwd block map");
+  e = msa::launch_sparse_bwd(P, a, m, w, s);
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_bwd launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -109,4 +109,27 @@ hipError_t launch_sparse_fwd(const Problem& P, const void* q, const void* k, con
                              const int32_t* block_idx, void* o, float* lse, const BlockMap& m,
                              void* partials, int chunk_queries, hipStream_t s);
 
+// Backward: caller tensors and the library's scratch.
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dO;
+  const float* lse;
+  const int32_t* block_idx;
+  const void *q_idx, *k_idx;
+  float kl_weight;
+  void *dq, *dk, *dv;
+  float *dq_idx, *dk_idx, *dscore, *kl;
+};
+struct BwdScratch {
+  float* D;            // [B, N, H_q]   rowsum(dO * O)
+  float2* idx_part;    // [B, N, H_kv, topk] per-slot (max, sum) of the index logits
+  float* lse_idx;      // [B, N, H_kv]  index log-sum-exp over the selected support
+  float* dq_acc;       // [B, N, H_q, d]  fp32
+  float* dk_acc;       // [B, N, H_kv, d] fp32
+  float* dv_acc;       // [B, N, H_kv, d] fp32
+};
+size_t sparse_bwd_scratch_bytes(const Problem& P);
+void sparse_bwd_scratch_carve(const Problem& P, void* ws, BwdScratch* w);
+hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w,
+                             hipStream_t s);
+
 }  // namespace msa
