@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the MiniMax Sparse Attention hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic inputs
+already resident in HBM: msa_index_topk (index scores, block max-pool,
+top-k), msa_sparse_fwd (block map, sparse attention, LSE merge) and, for the
+workloads that train, msa_sparse_bwd (fused main + KL index gradients).
+Default workload: B=1, N=131072, H_q=64, H_kv=8, d=128, d_idx=64, block 128,
+top-16, bf16, forward + backward.
+
+Prints ONE JSON line.  `roofline` describes the kernel with the largest time
+per step, timed live with hipEvents recorded by the library around each of
+its launches on the caller's stream; `cpu_baseline` times the fp64 oracle on
+a bounded sample of query rows on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MSA fwd+bwd tokens/s at N=128K; sparse-attn TFLOP/s as % of bf16 MFMA peak"
+
+# Source file of each kernel (the measured traffic of a kernel is only
+# reported while this file is unchanged since the counters were taken).
+KERNEL_SOURCE = {
+    "index_topk": "index_topk.hip",
+    "fwd_partial": "sparse_fwd.hip",
+    "fwd_merge": "sparse_fwd.hip",
+    "bwd_main": "sparse_bwd.hip",
+    "bwd_idx_lse": "sparse_bwd.hip",
+    "bwd_prep": "sparse_bwd.hip",
+    "bwd_finalize": "sparse_bwd.hip",
+    "block_map": "block_map.hip",
+    "block_items": "block_map.hip",
+}
+
+
+def support_pairs(N: int, block: int, topk: int) -> int:
+    """Sum over queries t of |S(t)|: causal, own block forced, every other
+    selected block fully visible -> min(k-1, t // block) * block + t % block + 1."""
+    t = np.arange(N, dtype=np.int64)
+    return int((np.minimum(topk - 1, t // block) * block + t % block + 1).sum())
+
+
+def algorithmic_work(w) -> dict:
+    """Algorithmic work of one launch of each kernel (flops or bytes)."""
+    pairs = support_pairs(w.N, w.block_size, w.topk) * w.B          # (t, u) pairs per group/head
+    esz = 2 if w.dtype == "bf16" else 4
+    vis = w.B * w.N * (w.N + 1) // 2                                # causally visible (t, u)
+    out = {
+        "index_topk": ("flop", 2.0 * w.d_idx * vis * w.H_kv),
+        "fwd_partial": ("flop", 4.0 * w.d * pairs * w.H_q),
+        "bwd_main": ("flop", (10.0 * w.d * w.H_q + 6.0 * w.d_idx * w.H_kv) * pairs),
+        "bwd_idx_lse": ("flop", 2.0 * w.d_idx * pairs * w.H_kv),
+        # merge: read topk partials (row + fp32 lse) per (t, h), write o and lse
+        "fwd_merge": ("byte", float(w.B * w.N * w.H_q * (w.topk * (w.d * esz + 4) + w.d * esz + 4))),
+    }
+    return out
+
+
+def source_sha(kernel: str) -> str | None:
+    f = KERNEL_SOURCE.get(kernel)
+    if f is None:
+        return None
+    path = os.path.join(ROOT, "block_sparse_attention_branch_amd", "csrc", f)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, rows_n: int, seed: int = 0) -> dict | None:
+    """Time the fp64 oracle (as it is) on `rows_n` query rows of batch 0:
+    index branch, forward and backward of those rows, on the host cores."""
+    if rows_n <= 0:
+        return None
+    from threadpoolctl import threadpool_info
+    from oracle import msa_oracle as O
+    import torch
+
+    rng = np.random.default_rng(seed)
+    ts = np.unique(np.concatenate([[0, w.N - 1], rng.integers(0, w.N, size=rows_n)]))[:rows_n]
+    rows = [(0, int(t)) for t in ts]
+    bt = torch.tensor(rows, dtype=torch.long)
+    f32 = lambda t: t.detach().float().cpu().numpy()
+    k, v, ki = f32(x["k"]), f32(x["v"]), f32(x["k_idx"])
+    q, qi = f32(x["q"][bt[:, 0], bt[:, 1]]), f32(x["q_idx"][bt[:, 0], bt[:, 1]])
+    dO = f32(x["dO"][bt[:, 0], bt[:, 1]]) if "dO" in x else None
+    t0 = time.perf_counter()
+    sel_rows = O.index_topk(qi, ki, w.block_size, w.topk, causal=w.causal, rows=rows)
+    sel = np.full((w.B, w.N, w.H_kv, w.topk), -1, dtype=np.int64)
+    for i, (b, t) in enumerate(rows):
+        sel[b, t] = sel_rows[i]
+    O.sparse_fwd(q, k, v, sel, w.block_size, w.causal, rows=rows)
+    if w.backward:
+        O.sparse_bwd(q, k, v, dO, qi, ki, sel, w.block_size, w.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    return {
+        "value": len(rows) / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(rows)} seeded query rows of batch 0 of {w.name} (every group and head): index "
+                   f"scores/max-pool/top-k, sparse forward" + (" and backward" if w.backward else "") +
+                   f" in fp64 NumPy, {dt:.1f} s"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fwdbwd-bf16-n128k")
+    ap.add_argument("--variant", default="normal", choices=["normal", "int", "planted"])
+    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows for the oracle baseline (0: skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_sparse_attention_branch_amd as msa
+    import msa_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    msa.load_library()
+    w = msa_inputs.WORKLOADS[args.workload]
+    x = msa_inputs.make_inputs(w, args.variant, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        sel = msa.index_topk(x["q_idx"], x["k_idx"], topk=w.topk, block_size=w.block_size, causal=w.causal)
+        o, lse = msa.sparse_fwd(x["q"], x["k"], x["v"], sel, d_idx=w.d_idx, block_size=w.block_size,
+                                causal=w.causal)
+        if w.backward:
+            msa.sparse_bwd(x["q"], x["k"], x["v"], o, x["dO"], lse, sel, x["q_idx"], x["k_idx"],
+                           block_size=w.block_size, causal=w.causal)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    msa.profile_enable(True)
+    msa.profile_collect()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = msa.profile_collect()
+    msa.profile_enable(False)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = w.B * w.N * args.steps / elapsed
+    work = algorithmic_work(w)
+    kernels = {}
+    for name, (launches, total_ms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
+        rec = {"ms_per_step": total_ms / args.steps, "launches_per_step": launches / args.steps}
+        if name in work:
+            kind, amount = work[name]
+            per_launch = amount / max(1, launches // args.steps)
+            avg_ms = total_ms / launches
+            if kind == "flop":
+                rec.update(achieved=per_launch / (avg_ms * 1e-3) / 1e12, unit="TFLOP/s")
+                rec["frac"] = rec["achieved"] / PEAK_BF16_TFLOPS
+            else:
+                rec.update(achieved=per_launch / (avg_ms * 1e-3) / 1e9, unit="GB/s")
+                rec["frac"] = rec["achieved"] / PEAK_HBM_GBS
+        kernels[name] = rec
+    dominant = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    launches, total_ms = prof[dominant]
+    kind, amount = work.get(dominant, ("flop", float("nan")))
+    per_launch = amount / max(1, launches // args.steps)
+    avg_ms = total_ms / launches
+    if kind == "flop":
+        achieved, peak, unit, bound = per_launch / (avg_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = per_launch / (avg_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                "traffic": measured_traffic(dominant, w.name), "kernel": dominant,
+                "avg_launch_ms": avg_ms, "work_per_launch": per_launch}
+
+    sparse_flop = work["fwd_partial"][1] + (work["bwd_main"][1] if w.backward else 0.0)
+    sparse_ms = sum(prof.get(n, (0, 0.0))[1] for n in ("block_map", "block_items", "fwd_partial", "fwd_merge",
+                                                        "bwd_prep", "bwd_idx_lse", "bwd_main", "bwd_finalize"))
+    sparse_ms /= args.steps
+    sparse_tflops = sparse_flop / (sparse_ms * 1e-3) / 1e12 if sparse_ms > 0 else None
+
+    cpu = cpu_baseline(w, x, args.cpu_rows)
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": f"synthetic ({args.variant}, seeded)",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H_q": w.H_q, "H_kv": w.H_kv, "d": w.d,
+                   "d_idx": w.d_idx, "block_size": w.block_size, "topk": w.topk, "causal": w.causal,
+                   "backward": w.backward, "parallelism": "single-gpu"},
+        "sparse_attn_tflops": sparse_tflops,
+        "sparse_attn_frac_of_bf16_peak": (sparse_tflops / PEAK_BF16_TFLOPS) if sparse_tflops else None,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

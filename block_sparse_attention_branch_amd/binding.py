@@ -30,6 +30,7 @@ EXPORTED = (
     "msa_sparse_fwd_workspace", "msa_sparse_fwd",
     "msa_sparse_bwd_workspace", "msa_sparse_bwd",
     "msa_status_string", "msa_last_error", "msa_version",
+    "msa_profile_enable", "msa_profile_collect",
 )
 
 
@@ -78,6 +79,11 @@ def load_library(path: str | None = None):
     lib.msa_last_error.restype = ctypes.c_char_p
     lib.msa_version.argtypes = []
     lib.msa_version.restype = i32
+    lib.msa_profile_enable.argtypes = [i32]
+    lib.msa_profile_enable.restype = i32
+    lib.msa_profile_collect.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i32),
+                                        ctypes.POINTER(ctypes.c_double)]
+    lib.msa_profile_collect.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -198,3 +204,20 @@ def sparse_bwd(q, k, v, o, dO, lse, block_idx, q_idx, k_idx, kl_weight: float = 
                             _stream(dev))
     _check(lib, st, "msa_sparse_bwd")
     return out
+
+
+def profile_enable(on: bool = True) -> None:
+    """Bracket every internal kernel launch with hipEvents (measurement only)."""
+    load_library().msa_profile_enable(int(bool(on)))
+
+
+def profile_collect(max_kernels: int = 64) -> dict:
+    """{kernel name: (launches, total ms)} since the previous collect."""
+    lib = load_library()
+    names = (ctypes.c_char_p * max_kernels)()
+    launches = (ctypes.c_int * max_kernels)()
+    total = (ctypes.c_double * max_kernels)()
+    n = lib.msa_profile_collect(max_kernels, names, launches, total)
+    if n < 0:
+        raise MsaError(n, "msa_profile_collect", lib.msa_last_error().decode())
+    return {names[i].decode(): (launches[i], total[i]) for i in range(n)}

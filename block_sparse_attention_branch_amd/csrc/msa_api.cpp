@@ -3,10 +3,14 @@
 // are documented in include/msa.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "msa_internal.h"
 
@@ -107,9 +111,100 @@ int fwd_chunk_queries(const msa::Problem& P) {
   return (int)q;
 }
 
+// Kernel timing (see msa_profile_enable in msa.h).
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_prof_pool;
+thread_local const char* t_prof_name = nullptr;
+thread_local hipEvent_t t_prof_start = nullptr;
+
+hipEvent_t prof_event() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
 
+namespace msa {
+
+void prof_begin(const char* name, hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  hipEvent_t e = prof_event();
+  if (e == nullptr) return;
+  (void)hipEventRecord(e, s);
+  t_prof_name = name;
+  t_prof_start = e;
+}
+
+void prof_end(hipStream_t s) {
+  if (t_prof_start == nullptr) return;
+  hipEvent_t e = prof_event();
+  if (e != nullptr) {
+    (void)hipEventRecord(e, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_records.push_back({t_prof_name, t_prof_start, e});
+  } else {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pool.push_back(t_prof_start);
+  }
+  t_prof_start = nullptr;
+}
+
+}  // namespace msa
+
 extern "C" {
+
+MSA_API int msa_profile_enable(int on) {
+  g_prof_on.store(on != 0);
+  return MSA_OK;
+}
+
+MSA_API int msa_profile_collect(int max, const char** names, int* launches, double* total_ms) {
+  if (max < 0 || (max > 0 && (names == nullptr || launches == nullptr || total_ms == nullptr)))
+    return fail(MSA_ERR_INVALID_ARG, "msa_profile_collect: bad output arrays");
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof_records);
+  }
+  int n = 0;
+  for (const ProfRecord& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      ms = 0.f;
+    int i = 0;
+    while (i < n && std::strcmp(names[i], r.name) != 0) ++i;
+    if (i == n) {
+      if (n == max) continue;
+      names[n] = r.name;
+      launches[n] = 0;
+      total_ms[n] = 0.0;
+      ++n;
+    }
+    launches[i] += 1;
+    total_ms[i] += ms;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (const ProfRecord& r : recs) {
+      g_prof_pool.push_back(r.start);
+      g_prof_pool.push_back(r.stop);
+    }
+  }
+  return n;
+}
 
 MSA_API int msa_version(void) { return 1; }
 

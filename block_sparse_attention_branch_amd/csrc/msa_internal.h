@@ -80,6 +80,12 @@ struct Problem {
 
 hipError_t launch_fill_f32(float* p, size_t n, float value, hipStream_t s);
 
+// Measurement hooks around kernel launches (no-ops unless timing is enabled
+// through msa_profile_enable).  Each prof_begin is closed by one prof_end on
+// the same thread and stream.
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
 hipError_t launch_index_topk(const Problem& P, const void* q_idx, const void* k_idx,
                              int32_t* block_idx, float* pooled, hipStream_t s);
 

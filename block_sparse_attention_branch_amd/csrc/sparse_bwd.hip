@@ -649,6 +649,7 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
   const size_t rows_q = (size_t)P.B * P.N * P.H_q;
   const size_t rows_g = (size_t)P.B * P.N * P.H_kv;
   // Zero every accumulator (fill kernels: safe inside captured graphs).
+  prof_begin("bwd_prep", s);
   if ((e = launch_fill_f32(w.dq_acc, rows_q * P.d, 0.f, s)) != hipSuccess) return e;
   if ((e = launch_fill_f32(w.dk_acc, rows_g * P.d, 0.f, s)) != hipSuccess) return e;
   if ((e = launch_fill_f32(w.dv_acc, rows_g * P.d, 0.f, s)) != hipSuccess) return e;
@@ -668,6 +669,7 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
                          static_cast<const bf16*>(a.dO), static_cast<const bf16*>(a.o), w.D, rows_q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  prof_end(s);
   // Work items over the whole sequence.
   if ((e = launch_block_items(P, m, 0, P.N, kItemQueries, s)) != hipSuccess) return e;
   size_t grid = block_items_upper_bound(P, 0, P.N, kItemQueries);
@@ -675,6 +677,7 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int n_lists = P.B * P.H_kv * P.nblk;
   // Index log-sum-exp over the selected support.
+  prof_begin("bwd_idx_lse", s);
   if (P.d_idx == 64)
     hipLaunchKernelGGL(idx_lse_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16*>(a.q_idx),
                        static_cast<const bf16*>(a.k_idx), a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.idx_part,
@@ -686,17 +689,23 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(idx_lse_merge_kernel, dim3((unsigned)((rows_g + 255) / 256)), dim3(256), 0, s, w.idx_part,
                      a.block_idx, w.lse_idx, rows_g, P.topk);
+  prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Fused main + index backward.
+  prof_begin("bwd_main", s);
   if (P.d == 128 && P.d_idx == 64) e = run_main_g<128, 64>(P, a, m, w, (int)grid, s);
   else if (P.d == 128) e = run_main_g<128, 32>(P, a, m, w, (int)grid, s);
   else if (P.d_idx == 64) e = run_main_g<64, 64>(P, a, m, w, (int)grid, s);
   else e = run_main_g<64, 32>(P, a, m, w, (int)grid, s);
+  prof_end(s);
   if (e != hipSuccess) return e;
   // fp32 accumulators to bf16 outputs.
+  prof_begin("bwd_finalize", s);
   if ((e = to_bf16(w.dq_acc, a.dq, rows_q * P.d, s)) != hipSuccess) return e;
   if ((e = to_bf16(w.dk_acc, a.dk, rows_g * P.d, s)) != hipSuccess) return e;
-  return to_bf16(w.dv_acc, a.dv, rows_g * P.d, s);
+  e = to_bf16(w.dv_acc, a.dv, rows_g * P.d, s);
+  prof_end(s);
+  return e;
 }
 
 }  // namespace msa

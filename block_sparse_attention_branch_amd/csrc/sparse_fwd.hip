@@ -320,15 +320,19 @@ hipError_t run_fwd(const Problem& P, const T* q, const T* k, const T* v, const i
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int s_lo = c0 / span;
     const int s_hi = (c1 == P.N) ? m.nsb : c1 / span;
+    prof_begin("fwd_partial", s);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kFwdThreads), C::LDS, s, q, k, v, block_idx, m.pos,
                        m.offs, m.rows, m.tiles, po, pl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, s_lo,
                        s_hi, c0, c1, n_lists, P.scale, (int)(grid / 8));
+    prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     constexpr int LPR = D / (16 / (int)sizeof(T));
     const size_t rows = (size_t)P.B * CQ * P.H_q;
     const size_t blocks = (rows + (256 / LPR) - 1) / (256 / LPR);
+    prof_begin("fwd_merge", s);
     hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, po, pl, block_idx, o,
                        lse, P.B, P.N, P.H_kv, P.G, P.topk, c0, CQ);
+    prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

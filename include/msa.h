@@ -178,6 +178,19 @@ MSA_API int msa_sparse_bwd(const msa_dims* dims, const void* q, const void* k, c
                            float* dq_idx, float* dk_idx, float* dscore, float* kl,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Kernel timing, for measurement only.  While enabled (process-wide), every
+ * entry point brackets each of its internal kernel launches with a pair of
+ * hipEvents recorded on the caller's stream; msa_profile_collect() waits for
+ * the recorded events and returns, per kernel name, the number of launches
+ * and their summed duration since the previous collect, then forgets them.
+ * Events come from a pool the library creates on first use and keeps.
+ * Returns the number of entries written (at most max), or a negative status.
+ * Disabled by default; costs nothing when disabled.
+ */
+MSA_API int msa_profile_enable(int on);
+MSA_API int msa_profile_collect(int max, const char** names, int* launches, double* total_ms);
+
 /* Text for a status code (static storage). */
 MSA_API const char* msa_status_string(int status);
 /* Detail of the last failing call on this thread ("" if none). */
