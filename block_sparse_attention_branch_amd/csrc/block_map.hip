@@ -218,12 +218,14 @@ hipError_t launch_block_map(const Problem& P, const int32_t* block_idx, const Bl
 // Work items of the KV-outer kernels for the query range [c0, c1): per list
 // (b, g, j) one diagonal item when block j lies in the range (its own 128
 // queries, causal mask) plus ceil(len / item_queries) items over the list
-// segment of the range.  tiles[] = exclusive scan over lists, tiles[n] = total.
+// segment of the range; with merge_diag the diagonal queries join the first
+// list item instead (at least one item per list in range).  tiles[] =
+// exclusive scan over lists, tiles[n] = total.
 namespace {
 __global__ __launch_bounds__(1024) void bm_items_kernel(const int32_t* __restrict__ pos,
                                                         int32_t* __restrict__ tiles, int nblk, int nsb,
                                                         int n_bg, int s_lo, int s_hi, int jb_lo, int jb_hi,
-                                                        int item_queries) {
+                                                        int item_queries, int merge_diag) {
   // Count items per list into tiles[], then scan in place (two passes over a
   // small array; one workgroup).
   const int n = n_bg * nblk;
@@ -232,7 +234,9 @@ __global__ __launch_bounds__(1024) void bm_items_kernel(const int32_t* __restric
     const int32_t* pb = pos + (size_t)bg * (nsb + 1) * nblk + j;
     const int len = pb[(size_t)s_hi * nblk] - pb[(size_t)s_lo * nblk];
     const int diag = (j >= jb_lo && j < jb_hi) ? 1 : 0;
-    tiles[i] = diag + (len + item_queries - 1) / item_queries;
+    const int lists = (len + item_queries - 1) / item_queries;
+    // merge_diag: the diagonal queries ride along with the first list item.
+    tiles[i] = merge_diag ? (diag ? max(1, lists) : lists) : diag + lists;
   }
   __syncthreads();
   // In-place exclusive scan with a one-workgroup pass over contiguous runs.
@@ -261,13 +265,13 @@ __global__ __launch_bounds__(1024) void bm_items_kernel(const int32_t* __restric
 }  // namespace
 
 hipError_t launch_block_items(const Problem& P, const BlockMap& m, int q_lo, int q_hi, int item_queries,
-                              hipStream_t s) {
+                              hipStream_t s, int merge_diag) {
   const int n_bg = P.B * P.H_kv;
   const int s_lo = q_lo / (m.SB * kBlock);
   const int s_hi = (q_hi == P.N) ? m.nsb : q_hi / (m.SB * kBlock);
   prof_begin("block_items", s);
   hipLaunchKernelGGL(bm_items_kernel, dim3(1), dim3(1024), 0, s, m.pos, m.tiles, P.nblk, m.nsb, n_bg, s_lo,
-                     s_hi, q_lo / kBlock, (q_hi + kBlock - 1) / kBlock, item_queries);
+                     s_hi, q_lo / kBlock, (q_hi + kBlock - 1) / kBlock, item_queries, merge_diag);
   prof_end(s);
   return hipGetLastError();
 }

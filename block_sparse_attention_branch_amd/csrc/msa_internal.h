@@ -106,7 +106,7 @@ hipError_t launch_block_map(const Problem& P, const int32_t* block_idx, const Bl
 // Work items of the KV-outer kernels for queries [q_lo, q_hi) (q_lo a
 // multiple of the super-block span).
 hipError_t launch_block_items(const Problem& P, const BlockMap& m, int q_lo, int q_hi,
-                              int item_queries, hipStream_t s);
+                              int item_queries, hipStream_t s, int merge_diag = 0);
 size_t block_items_upper_bound(const Problem& P, int q_lo, int q_hi, int item_queries);
 int block_map_super_span(const Problem& P);  // queries per super-block
 

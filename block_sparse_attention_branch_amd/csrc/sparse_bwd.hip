@@ -204,67 +204,144 @@ __global__ __launch_bounds__(256) void idx_lse_merge_kernel(const float2* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Main fused backward.  16x16x32 MFMA tiles: a 16x16 output D[m][n] lives in
-// 4 fp32 slots per lane, lane l holding column n = l % 16 and rows
-// m = 4*(l/16) + v (checked on gfx950 hardware); A-operand lane l holds row
-// l % 16, B-operand lane l column l % 16, both with k = 8*(l/16) + i.
+// Main fused backward.  4 waves; wave w owns keys 32w..32w+31 of the block.
+// 32x32x16 MFMA tiles (C-layout: lane l holds column l % 32, rows
+// 8*(v/4) + 4*(l/32) + v%4 in slot v; A/B operands: lane l holds row/column
+// l % 32 and k = 8*(l/32) + i).  Per step of 32 (query, head) rows:
+//   S = Q K_w^T, dP = dO V_w^T          (A from LDS tiles, B in registers)
+//   P, dS                               (lane = key, slots = rows)
+//   dV_w^T += dO^T P, dK_w^T += Q^T dS  (A from transposed LDS tiles, B = the
+//                                        P / dS registers as they are)
+//   index logits, p_px, teacher, dz, dk_idx_w^T += q_idx^T dz
+//   dQ[:, 32w..32w+31] = dS K, dq_idx = dz K_idx  (K^T / K_idx^T operands of
+//                                        the wave's output columns in registers)
 // ---------------------------------------------------------------------------
-constexpr int kBwdWaves = 8;
+constexpr int kBwdWaves = 4;
 constexpr int kMainThreads = kBwdWaves * kWave;
+
+// Work items of the main kernel: the queries of KV block j (its own 128, with
+// the causal mask) together with the first kBigItem entries of its inverted
+// list, or a later run of kBigItem list entries.  Long items keep the
+// per-item flush of dK, dV and dk_idx rare.
+constexpr int kBigItem = 1024;
 
 template <int D, int DIDX>
 struct BwdCfg {
   static constexpr int PKT = kBlock + 8;   // rows of 128 keys (+16 B)
   static constexpr int PQ = D + 8;         // Q / dO rows (+16 B)
   static constexpr int PQI = DIDX + 8;     // q_idx rows (+16 B)
-  static constexpr int PR = 32 + 8;        // transposed tiles: rows of 32 (+16 B)
-  static constexpr size_t OFF_KT = 0;                                   // K^T      [D][PKT]
-  static constexpr size_t OFF_KIT = OFF_KT + (size_t)D * PKT * 2;       // K_idx^T  [DIDX][PKT]
-  static constexpr size_t OFF_QS = OFF_KIT + (size_t)DIDX * PKT * 2;    // Q        [32][PQ]
+  static constexpr size_t OFF_QS = 0;                                   // Q        [32][PQ]
   static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;       // dO       [32][PQ]
-  static constexpr size_t OFF_QT = OFF_DOS + (size_t)32 * PQ * 2;       // Q^T      [D][PR]
-  static constexpr size_t OFF_DOT = OFF_QT + (size_t)D * PR * 2;        // dO^T     [D][PR]
-  static constexpr size_t OFF_QIS = OFF_DOT + (size_t)D * PR * 2;       // q_idx    [32][PQI]
-  static constexpr size_t OFF_QIT = OFF_QIS + (size_t)32 * PQI * 2;     // q_idx^T  [DIDX][PR]
-  static constexpr size_t OFF_DS = OFF_QIT + (size_t)DIDX * PR * 2;     // dS       [32][PKT]
+  static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;      // q_idx    [32][PQI]
+  static constexpr size_t OFF_DS = OFF_QIS + (size_t)32 * PQI * 2;      // dS       [32][PKT]
   static constexpr size_t OFF_DZ = OFF_DS + (size_t)32 * PKT * 2;       // dz       [32][PKT]
   static constexpr size_t OFF_PB = OFF_DZ + (size_t)32 * PKT * 2;       // P        [32][128] fp32
-  static constexpr size_t OFF_TAB = OFF_PB + (size_t)32 * kBlock * 4;   // 2 x row/query tables
-  static constexpr int TAB_WORDS = 10 * 32;
-  static constexpr size_t LDS = OFF_TAB + 2 * TAB_WORDS * 4;
+  static constexpr size_t OFF_TAB = OFF_PB + (size_t)32 * kBlock * 4;   // 2 x 10 x [32] step tables
+  static constexpr size_t OFF_KIT = OFF_TAB + 2 * 10 * 32 * 4;          // K_idx^T  [DIDX][PKT]
+  static constexpr size_t OFF_QL = OFF_KIT + (size_t)DIDX * PKT * 2;    // item queries: (t << 6) | slot
+  static constexpr size_t LDS = OFF_QL + (size_t)(kBlock + kBigItem) * 4;
+  // The flush at the end of an item reuses [OFF_DS, OFF_TAB) as 4 x [32][33] fp32.
+  static_assert(OFF_TAB - OFF_DS >= 4 * 32 * 33 * 4, "flush scratch");
 };
 
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
+// A work item of the main kernel and the queries it covers: item-local query
+// qi < n_own is t = 128 j + qi (diagonal, causal mask); otherwise it is list
+// entry e0 + qi - n_own of block j's inverted list.
+struct BigItem {
+  int b, g, j, n_own, ne, e0;
+  const int32_t* ent;
+};
 
-__device__ inline f4 mma16(bf16x8 a, bf16x8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ inline bool decode_big_item(const int32_t* __restrict__ tiles, const int32_t* __restrict__ pos,
+                                       const int32_t* __restrict__ offs, const int32_t* __restrict__ rows,
+                                       int n_lists, int per_xcd, int N, int H_kv, int topk, int nblk, int nsb,
+                                       BigItem* it) {
+  const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (w >= tiles[n_lists]) return false;
+  int lo = 0, hi = n_lists - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tiles[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  const int li = w - tiles[lo];
+  it->j = lo % nblk;
+  const int bg = lo / nblk;
+  it->g = bg % H_kv;
+  it->b = bg / H_kv;
+  const int len = pos[((size_t)bg * (nsb + 1) + nsb) * nblk + it->j];
+  it->n_own = li == 0 ? kBlock : 0;
+  it->e0 = li * kBigItem;
+  it->ne = max(0, min(kBigItem, len - it->e0));
+  it->ent = rows + (size_t)bg * N * topk + offs[(size_t)bg * (nblk + 1) + it->j];
+  return true;
 }
-__device__ inline f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
-// A operand from a transposed [m][32 rows] LDS tile whose K (rows) follow
-// the C-layout of two stacked 16-row tiles: lane l, slot i <-> row
-// 4*(l/16) + i for i < 4 and 16 + 4*(l/16) + i - 4 otherwise.
-__device__ inline bf16x8 tfrag16(const bf16* base, int pitch, int m, int lane) {
-  const bf16* p = base + m * pitch + 4 * (lane >> 4);
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+// t (-1 when qi is past the item), visibility cut-off (key u is visible iff
+// u <= cut) and, when asked, the slot of block j in the query's row.
+__device__ inline int big_query(const BigItem& it, int qi, const int32_t* __restrict__ block_idx, int N, int H_kv,
+                                int topk, int causal, bool want_slot, int* cut, int* slot) {
+  *slot = 0;
+  *cut = -1;
+  if (qi < it.n_own) {
+    const int t = it.j * kBlock + qi;
+    *cut = causal ? t : 0x7fffffff;
+    if (want_slot) {
+      const int32_t* brow = block_idx + (((size_t)it.b * N + t) * H_kv + it.g) * topk;
+      for (int e = 0; e < topk; ++e)
+        if (brow[e] == it.j) *slot = e;
+    }
+    return t;
+  }
+  const int ei = qi - it.n_own;
+  if (ei >= it.ne) return -1;
+  const int e = it.ent[it.e0 + ei];
+  const int t = e >> 6;
+  if (t < 0 || t >= N || (e & 63) >= topk) return -1;   // malformed map: drop the entry
+  *slot = e & 63;
+  *cut = 0x7fffffff;
+  return t;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// A operand X^T of a 32x32x16 MFMA read straight from a row-major [rows][cols]
+// bf16 LDS tile with the gfx950 transpose read (within each group of 16
+// lanes, lane i receives element i % 4 of the vectors addressed by lanes
+// 4k + i / 4, k = 0..3; checked on hardware): lane l gets column m0 + l % 32
+// and the K values of rows r0 .. r0+3 (slots 0..3) and r0+8 .. r0+11
+// (slots 4..7), with r0 = 16 kc + 4 (l / 32) - the row order of a C-layout
+// tile's slots 8 kc .. 8 kc + 7.
+__device__ inline bf16x8 trfrag(const bf16* base, int pitch, int m0, int kc, int lane) {
+  const int jj = lane & 15;
+  const int r0 = 16 * kc + 4 * (lane >> 5) + (jj >> 2);
+  const int col = m0 + 16 * ((lane >> 4) & 1) + 4 * (jj & 3);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + r0 * pitch + col));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + (r0 + 8) * pitch + col));
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
   bf16x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  r[0] = l4[0]; r[1] = l4[1]; r[2] = l4[2]; r[3] = l4[3];
+  r[4] = h4[0]; r[5] = h4[1]; r[6] = h4[2]; r[7] = h4[3];
   return r;
 }
-// Matching B operand from two stacked 16-row C-layout tiles.
-__device__ inline bf16x8 cfrag16(const f4& x0, const f4& x1) {
+// Matching B operand: slots 8kc .. 8kc+7 of a C-layout tile.
+__device__ inline bf16x8 cfrag(const f32x16& x, int kc) {
   bf16x8 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (bf16)x0[i];
-    r[i + 4] = (bf16)x1[i];
-  }
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)x[8 * kc + i];
   return r;
 }
+__device__ inline f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// Add a C-layout column (lane = output row, slots = 16 consecutive-by-group
+// columns 8 (v/4) + v%4 past `base`, which already includes 4 (l/32)).
+__device__ inline void atomic_add_col(float* base, const f32x16& x) {
+#pragma unroll
+  for (int vv = 0; vv < 16; ++vv) atomicAdd(base + 8 * (vv >> 2) + (vv & 3), x[vv]);
+}
 
-template <int D, int DIDX, int G>
+template <int D, int DIDX, int G, bool EXTRA>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dv,
@@ -275,295 +352,346 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     float* __restrict__ dk_idx, float* __restrict__ dscore, float* __restrict__ kl, int N, int H_kv, int topk,
     int causal, int nblk, int nsb, int n_lists, float scale, float scale_idx, float lam, int per_xcd) {
   using C = BwdCfg<D, DIDX>;
-  constexpr int KS = D / 32;        // k-steps over d
-  constexpr int KSI = DIDX / 32;    // k-steps over d_idx
-  constexpr int DT = D / 16;        // 16-wide d tiles
-  constexpr int DTI = DIDX / 16;    // 16-wide d_idx tiles
+  constexpr int KS = D / 16;        // 16-wide k-steps over d
+  constexpr int KSI = DIDX / 16;    // 16-wide k-steps over d_idx
+  constexpr int DT = D / 32;        // 32-wide d tiles
+  constexpr int DTI = DIDX / 32;    // 32-wide d_idx tiles
   constexpr int TQ = 32 / G;        // queries per 32-row step
-  constexpr int MQ = TQ > 16 ? 2 : 1;
-  constexpr int NT_Q = 2 * DT;      // dQ output tiles per step
-  constexpr int NT = NT_Q + MQ * DTI;
+  constexpr int KCQ = TQ > 16 ? 2 : 1;                     // 16-query chunks holding real queries
+  constexpr int NVQ = TQ <= 8 ? 4 : (TQ <= 16 ? 8 : 16);   // slots that can hold a query < TQ
+  constexpr int CPR = D / 8;        // 16-byte chunks per Q / dO row
+  constexpr int CPRI = DIDX / 8;    // 16-byte chunks per q_idx row
+  constexpr int LDM = 32 * CPR / kMainThreads;              // Q (and dO) chunks per thread
+  static_assert(32 * CPR % kMainThreads == 0, "tile split");
+  static_assert(32 * CPRI <= kMainThreads, "q_idx tile split");
+  static_assert(DT <= kBwdWaves, "one dQ column tile per wave");
   extern __shared__ __align__(16) char smem[];
-  bf16* Kt = reinterpret_cast<bf16*>(smem + C::OFF_KT);
-  bf16* KIt = reinterpret_cast<bf16*>(smem + C::OFF_KIT);
   bf16* Qs = reinterpret_cast<bf16*>(smem + C::OFF_QS);
   bf16* dOs = reinterpret_cast<bf16*>(smem + C::OFF_DOS);
-  bf16* Qt = reinterpret_cast<bf16*>(smem + C::OFF_QT);
-  bf16* dOt = reinterpret_cast<bf16*>(smem + C::OFF_DOT);
   bf16* QIs = reinterpret_cast<bf16*>(smem + C::OFF_QIS);
-  bf16* QIt = reinterpret_cast<bf16*>(smem + C::OFF_QIT);
   bf16* dSs = reinterpret_cast<bf16*>(smem + C::OFF_DS);
   bf16* dZs = reinterpret_cast<bf16*>(smem + C::OFF_DZ);
   float* Pb = reinterpret_cast<float*>(smem + C::OFF_PB);
-  int* tab0 = reinterpret_cast<int*>(smem + C::OFF_TAB);
+  int* tabs = reinterpret_cast<int*>(smem + C::OFF_TAB);        // [2][10][32]
+  bf16* KIt = reinterpret_cast<bf16*>(smem + C::OFF_KIT);
 
-  Item it;
-  if (!decode_item(tiles, pos, offs, rows, n_lists, per_xcd, N, H_kv, topk, nblk, nsb, &it)) return;
+  BigItem it;
+  if (!decode_big_item(tiles, pos, offs, rows, n_lists, per_xcd, N, H_kv, topk, nblk, nsb, &it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nn = lane & 15, qg = lane >> 4;
+  const int n = lane & 31, hf = lane >> 5;
   const int H_q = H_kv * G;
   const int b = it.b, g = it.g, j = it.j;
-  const int key = 16 * wave + nn;                     // this lane's key inside the block
+  const int key = 32 * wave + n;                      // this lane's key inside the block
   const int u = j * kBlock + key;
   const size_t kv_row = ((size_t)b * N + u) * H_kv + g;
+  const size_t blk_row0 = ((size_t)b * N + (size_t)j * kBlock) * H_kv + g;   // key 0 of the block
+  const int nq = it.n_own + it.ne;
+  const bool want_slot = EXTRA && dscore != nullptr;
+  int* qlist = reinterpret_cast<int*>(smem + C::OFF_QL);   // (t << 6) | slot, or -1
 
-  // K^T and K_idx^T of the block (B operands of dQ and dq_idx).
-  for (int c = threadIdx.x; c < kBlock * (D / 8); c += kMainThreads) {
-    const int kk = c / (D / 8), col = (c % (D / 8)) * 8;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(k + (((size_t)b * N + j * kBlock + kk) * H_kv + g) * D + col);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Kt[(col + i) * C::PKT + kk] = x[i];
+  // The item's queries in LDS, so that the step loop needs no dependent
+  // global load (the vector-memory counter is in order: a wait on a
+  // dependent load would also wait for the previous step's atomics).
+  for (int qi = threadIdx.x; qi < nq; qi += kMainThreads) {
+    int cut, slot;
+    const int t = big_query(it, qi, block_idx, N, H_kv, topk, causal, want_slot, &cut, &slot);
+    qlist[qi] = t < 0 ? -1 : ((t << 6) | slot);
   }
+  // K_idx^T of the block in LDS (B operand of dq_idx).
   for (int c = threadIdx.x; c < kBlock * (DIDX / 8); c += kMainThreads) {
     const int kk = c / (DIDX / 8), col = (c % (DIDX / 8)) * 8;
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
 #pragma unroll
     for (int i = 0; i < 8; ++i) KIt[(col + i) * C::PKT + kk] = x[i];
   }
-  // This wave's 16 keys as B operands (lane = key, K = d), in registers.
-  bf16x8 kf[KS], vf[KS], kif[KSI];
+  // Register operands for the whole item: this wave's 32 keys of K, V, K_idx
+  // (B of S, dP, r: lane = key, K = d), and K^T of the wave's 32 dQ columns
+  // (B of dQ: lane = column, K = keys).
+  bf16x8 kf[KS], vf[KS], kif[KSI], ktf[8];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = *reinterpret_cast<const bf16x8*>(k + kv_row * D + 32 * ks + 8 * qg);
-    vf[ks] = *reinterpret_cast<const bf16x8*>(v + kv_row * D + 32 * ks + 8 * qg);
+    kf[ks] = *reinterpret_cast<const bf16x8*>(k + kv_row * D + 16 * ks + 8 * hf);
+    vf[ks] = *reinterpret_cast<const bf16x8*>(v + kv_row * D + 16 * ks + 8 * hf);
   }
 #pragma unroll
   for (int ks = 0; ks < KSI; ++ks)
-    kif[ks] = *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + u) * DIDX + 32 * ks + 8 * qg);
+    kif[ks] = *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + u) * DIDX + 16 * ks + 8 * hf);
+  const int qcol = 32 * wave + n;                     // dQ column (wave < DT)
+  const bool has_q = DT == kBwdWaves || wave < DT;
+  // dq_idx: output tile wave % DTI, over keys [kpart * KPW, (kpart + 1) * KPW)
+  // of the block, so every wave issues the same atomics.
+  constexpr int KPARTS = kBwdWaves / DTI;
+  constexpr int KCW = 8 / KPARTS;                     // 16-key chunks per wave
+  const int itile = wave % DTI, kpart = wave / DTI;
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 16 * kc + 8 * hf + i;
+      ktf[kc][i] = has_q ? k[(blk_row0 + (size_t)kk * H_kv) * D + qcol] : (bf16)0.f;
+    }
 
-  f4 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
+  f32x16 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
 #pragma unroll
   for (int i = 0; i < DT; ++i) {
-    acc_dv[i] = zero4();
-    acc_dk[i] = zero4();
+    acc_dv[i] = zero16();
+    acc_dk[i] = zero16();
   }
 #pragma unroll
-  for (int i = 0; i < DTI; ++i) acc_dki[i] = zero4();
+  for (int i = 0; i < DTI; ++i) acc_dki[i] = zero16();
+  __syncthreads();   // item query list and K_idx^T ready
+
+  // Per-thread share of a step, loaded one step ahead into registers: LDM
+  // 16-byte chunks of Q and dO (with LSE, D and the cut-off of rows whose
+  // first chunk it holds), one chunk of q_idx, and - for threads < TQ - the
+  // step's query table entry (t, slot, cut-off, index LSE).
+  bf16x8 pre_q[LDM], pre_d[LDM], pre_qi = bf16x8{};
+  float pre_lse[LDM], pre_D[LDM], pre_qlse = 0.f;
+  int pre_t[LDM], pre_cut[LDM], pre_qt = -1, pre_qslot = 0, pre_qcut = -1;
+  const int ld_col = (threadIdx.x % CPR) * 8;
+  const int ld_qr = threadIdx.x / CPRI, ld_qcol = (threadIdx.x % CPRI) * 8;
+  const bool ld_idx = threadIdx.x < 32 * CPRI;
+  // Query qi of the item: t (-1 past the end), slot, visibility cut-off.
+  auto query = [&](int qi, int* slot, int* cut) {
+    const int e = qi < nq ? qlist[qi] : -1;
+    const int t = e < 0 ? -1 : (e >> 6);
+    *slot = e < 0 ? 0 : (e & 63);
+    *cut = t < 0 ? -1 : ((qi < it.n_own && causal) ? t : 0x7fffffff);
+    return t;
+  };
+  // Every load below is unconditional (clamped to a valid row) so that the
+  // compiler can count them exactly and later wait for them without also
+  // waiting for the atomics issued after them.
+  auto load_step = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < LDM; ++c) {
+      const int r = (threadIdx.x + c * kMainThreads) / CPR;
+      int slot;
+      pre_t[c] = query((32 * st + r) / G, &slot, &pre_cut[c]);
+      const size_t qrow = ((size_t)b * N + (pre_t[c] < 0 ? 0 : pre_t[c])) * H_q + g * G + r % G;
+      pre_q[c] = *reinterpret_cast<const bf16x8*>(q + qrow * D + ld_col);
+      pre_d[c] = *reinterpret_cast<const bf16x8*>(dO + qrow * D + ld_col);
+      pre_lse[c] = lse[qrow];
+      pre_D[c] = Dv[qrow];
+    }
+    {
+      int cut, slot;
+      const int qr = ld_qr < 32 ? ld_qr : 31;
+      const int tq = qr < TQ ? query(st * TQ + qr, &slot, &cut) : -1;
+      pre_qi = *reinterpret_cast<const bf16x8*>(q_idx + (((size_t)b * N + (tq < 0 ? 0 : tq)) * H_kv + g) * DIDX +
+                                                ld_qcol);
+      if (tq < 0) pre_qi = bf16x8{};
+    }
+    {
+      const int x = threadIdx.x & 31;
+      pre_qt = x < TQ ? query(st * TQ + x, &pre_qslot, &pre_qcut) : -1;
+      pre_qlse = lse_idx[((size_t)b * N + (pre_qt < 0 ? 0 : pre_qt)) * H_kv + g];
+    }
+  };
 
   const float c_s = scale * kLog2e;
   const float c_i = scale_idx * kLog2e;
-  const int n_steps = (it.nq * G + 31) / 32;
+  const int n_steps = (nq * G + 31) / 32;
+  // Store a step's prefetched registers into its LDS tiles and step tables
+  // (rows: t or -1, cut-off, LSE * log2(e), D; queries: t or -1, slot,
+  // cut-off, index LSE * log2(e), KL partial).
+  auto store_step = [&](int st) {
+    int* tb = tabs + (st & 1) * 320;
+#pragma unroll
+    for (int c = 0; c < LDM; ++c) {
+      const int r = (threadIdx.x + c * kMainThreads) / CPR;
+      *reinterpret_cast<bf16x8*>(Qs + r * C::PQ + ld_col) = pre_q[c];
+      *reinterpret_cast<bf16x8*>(dOs + r * C::PQ + ld_col) = pre_d[c];
+      if (ld_col == 0) {
+        tb[r] = pre_t[c];
+        tb[32 + r] = pre_t[c] < 0 ? -1 : pre_cut[c];
+        reinterpret_cast<float*>(tb)[64 + r] = pre_lse[c] * kLog2e;
+        reinterpret_cast<float*>(tb)[96 + r] = pre_D[c];
+      }
+    }
+    if (ld_idx) *reinterpret_cast<bf16x8*>(QIs + ld_qr * C::PQI + ld_qcol) = pre_qi;
+    if (threadIdx.x < 32) {
+      tb[128 + threadIdx.x] = pre_qt;
+      tb[160 + threadIdx.x] = pre_qslot;
+      tb[192 + threadIdx.x] = pre_qt < 0 ? -1 : pre_qcut;
+      reinterpret_cast<float*>(tb)[224 + threadIdx.x] = pre_qlse * kLog2e;
+      reinterpret_cast<float*>(tb)[256 + threadIdx.x] = 0.f;
+    }
+  };
+  load_step(0);
+  store_step(0);
 #pragma unroll 1
   for (int st = 0; st < n_steps; ++st) {
     asm volatile("" ::: "memory");
-    int* tab = tab0 + (st & 1) * C::TAB_WORDS;
-    int* row_t = tab;                                        // t of row, -1 if invalid
-    int* row_h = tab + 32;                                   // head of row
-    float* row_lse = reinterpret_cast<float*>(tab + 64);     // LSE * log2(e)
-    float* row_d = reinterpret_cast<float*>(tab + 96);       // D
-    int* qry_t = tab + 128;                                  // t of query, -1 if invalid
-    int* qry_slot = tab + 160;
-    float* qry_lse = reinterpret_cast<float*>(tab + 192);    // lse_idx * log2(e)
-    float* qry_kl = reinterpret_cast<float*>(tab + 224);
+    int* tb = tabs + (st & 1) * 320;
+    int* row_t = tb;
+    int* row_cut = tb + 32;
+    float* row_lse = reinterpret_cast<float*>(tb + 64);
+    float* row_d = reinterpret_cast<float*>(tb + 96);
+    int* qry_t = tb + 128;
+    int* qry_slot = tb + 160;
+    int* qry_cut = tb + 192;
+    float* qry_lse = reinterpret_cast<float*>(tb + 224);
+    float* qry_kl = reinterpret_cast<float*>(tb + 256);
+    __syncthreads();   // step st's tiles and tables in LDS
+    // Prefetch step st + 1 (past the end it re-reads valid rows, unused).
+    load_step(st + 1);
 
-    // (a) row and query tables.
-    if (wave == 0) {
-      const int x = lane & 31;
-      if (lane < 32) {
-        const int r = 32 * st + x;
-        int t, slot;
-        bool valid;
-        item_query(it, r / G, block_idx, N, H_kv, topk, &t, &slot, &valid);
-        const int h = g * G + x % G;
-        const size_t qrow = ((size_t)b * N + t) * H_q + h;
-        row_t[x] = valid ? t : -1;
-        row_h[x] = h;
-        row_lse[x] = lse[qrow] * kLog2e;
-        row_d[x] = Dv[qrow];
-      } else {
-        int t = 0, slot = 0;
-        bool valid = false;
-        if (x < TQ) item_query(it, st * TQ + x, block_idx, N, H_kv, topk, &t, &slot, &valid);
-        qry_t[x] = valid ? t : -1;
-        qry_slot[x] = slot;
-        qry_lse[x] = lse_idx[((size_t)b * N + t) * H_kv + g] * kLog2e;
-        qry_kl[x] = 0.f;
+    // (c) S, dP, index logits (lane = key, slots = rows / queries); P, dS;
+    // dV^T += dO^T P and dK^T += Q^T dS.
+    f32x16 s = zero16(), dp = zero16(), ri = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mma32(*reinterpret_cast<const bf16x8*>(Qs + n * C::PQ + 16 * ks + 8 * hf), kf[ks], s);
+      dp = mma32(*reinterpret_cast<const bf16x8*>(dOs + n * C::PQ + 16 * ks + 8 * hf), vf[ks], dp);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks)
+      ri = mma32(*reinterpret_cast<const bf16x8*>(QIs + n * C::PQI + 16 * ks + 8 * hf), kif[ks], ri);
+    f32x16 p, ds;
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int r4 = 8 * grp + 4 * hf;                 // rows r4 .. r4+3 = slots 4grp .. 4grp+3
+      const int4 cut = *reinterpret_cast<const int4*>(row_cut + r4);
+      const float4 l2 = *reinterpret_cast<const float4*>(row_lse + r4);
+      const float4 dd = *reinterpret_cast<const float4*>(row_d + r4);
+      const int cuts[4] = {cut.x, cut.y, cut.z, cut.w};
+      const float l2s[4] = {l2.x, l2.y, l2.z, l2.w};
+      const float dds[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int vv = 4 * grp + e;
+        const float pv = u <= cuts[e] ? __builtin_amdgcn_exp2f(s[vv] * c_s - l2s[e]) : 0.f;
+        p[vv] = pv;
+        ds[vv] = pv * (dp[vv] - dds[e]) * scale;
+        Pb[(r4 + e) * kBlock + key] = pv;
+        dSs[(r4 + e) * C::PKT + key] = (bf16)ds[vv];
       }
     }
-    __syncthreads();
-    // (b) Q, dO (32 rows) and q_idx (TQ rows) into LDS, row-major and transposed.
-    for (int c = threadIdx.x; c < 32 * (D / 8); c += kMainThreads) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int tr = row_t[r];
-      const size_t qrow = ((size_t)b * N + (tr < 0 ? 0 : tr)) * H_q + row_h[r];
-      const bf16x8 xq = *reinterpret_cast<const bf16x8*>(q + qrow * D + col);
-      const bf16x8 xd = *reinterpret_cast<const bf16x8*>(dO + qrow * D + col);
-      *reinterpret_cast<bf16x8*>(Qs + r * C::PQ + col) = xq;
-      *reinterpret_cast<bf16x8*>(dOs + r * C::PQ + col) = xd;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        Qt[(col + i) * C::PR + r] = xq[i];
-        dOt[(col + i) * C::PR + r] = xd[i];
-      }
-    }
-    for (int c = threadIdx.x; c < 32 * (DIDX / 8); c += kMainThreads) {
-      const int r = c / (DIDX / 8), col = (c % (DIDX / 8)) * 8;
-      const int tq = qry_t[r];
-      bf16x8 x = bf16x8{};
-      if (tq >= 0) x = *reinterpret_cast<const bf16x8*>(q_idx + (((size_t)b * N + tq) * H_kv + g) * DIDX + col);
-      *reinterpret_cast<bf16x8*>(QIs + r * C::PQI + col) = x;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) QIt[(col + i) * C::PR + r] = x[i];
-    }
-    __syncthreads();
-
-    // (c) S = Q K_w^T, dP = dO V_w^T (lane = key, slots = rows 16 mt + 4 qg + v),
-    // P, dS, then dV^T += dO^T P and dK^T += Q^T dS for this wave's 16 keys.
-    f4 s[2], dp[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = zero4();
-      dp[mt] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + (16 * mt + nn) * C::PQ + 32 * ks + 8 * qg);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dOs + (16 * mt + nn) * C::PQ + 32 * ks + 8 * qg);
-        s[mt] = mma16(aq, kf[ks], s[mt]);
-        dp[mt] = mma16(ad, vf[ks], dp[mt]);
-      }
-    }
-    f4 ri[MQ];
-#pragma unroll
-    for (int mt = 0; mt < MQ; ++mt) {
-      ri[mt] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KSI; ++ks)
-        ri[mt] = mma16(*reinterpret_cast<const bf16x8*>(QIs + (16 * mt + nn) * C::PQI + 32 * ks + 8 * qg), kif[ks],
-                       ri[mt]);
-    }
-    f4 p[2], ds[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int r = 16 * mt + 4 * qg + vv;
-        const int tr = row_t[r];
-        const bool vis = tr >= 0 && !(it.diag && causal && u > tr);
-        const float pv = vis ? exp2f(s[mt][vv] * c_s - row_lse[r]) : 0.f;
-        p[mt][vv] = pv;
-        ds[mt][vv] = pv * (dp[mt][vv] - row_d[r]) * scale;
-        Pb[r * kBlock + key] = pv;
-        dSs[r * C::PKT + key] = (bf16)ds[mt][vv];
-      }
-    {
-      const bf16x8 pb = cfrag16(p[0], p[1]), sb = cfrag16(ds[0], ds[1]);
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 pb = cfrag(p, kc), sb = cfrag(ds, kc);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        acc_dv[dt] = mma16(tfrag16(dOt, C::PR, 16 * dt + nn, lane), pb, acc_dv[dt]);
-        acc_dk[dt] = mma16(tfrag16(Qt, C::PR, 16 * dt + nn, lane), sb, acc_dk[dt]);
+        acc_dv[dt] = mma32(trfrag(dOs, C::PQ, 32 * dt, kc, lane), pb, acc_dv[dt]);
+        acc_dk[dt] = mma32(trfrag(Qs, C::PQ, 32 * dt, kc, lane), sb, acc_dk[dt]);
       }
     }
     __syncthreads();   // P of every head of a query visible to the teacher; dS complete
 
     // (d) Index branch on the query slots: p_px, teacher pbar, dz.
-    f4 dz[2];
-    dz[0] = zero4();
-    dz[1] = zero4();
-    float klv[MQ][4];
+    f32x16 dz = zero16();
 #pragma unroll
-    for (int mt = 0; mt < MQ; ++mt)
+    for (int vv = 0; vv < NVQ; ++vv) {
+      const int qr = c_row(vv, lane);
+      float klv = 0.f;
+      if (qr < TQ) {
+        const int tqq = qry_t[qr];
+        if (u <= qry_cut[qr]) {
+          const float lz = ri[vv] * c_i - qry_lse[qr];   // log2 p_px
+          const float ppx = __builtin_amdgcn_exp2f(lz);
+          float pbar = 0.f;
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int qr = 16 * mt + 4 * qg + vv;
-        klv[mt][vv] = 0.f;
-        if (qr < TQ) {
-          const int tqq = qry_t[qr];
-          if (tqq >= 0 && !(it.diag && causal && u > tqq)) {
-            const float lz = ri[mt][vv] * c_i - qry_lse[qr];   // log2 p_px
-            const float ppx = exp2f(lz);
-            float pbar = 0.f;
-#pragma unroll
-            for (int e = 0; e < G; ++e) pbar += Pb[(qr * G + e) * kBlock + key];
-            pbar *= 1.0f / G;
-            dz[mt][vv] = lam * (ppx - pbar);
-            if (kl != nullptr && pbar > 0.f) klv[mt][vv] = pbar * (logf(pbar) - lz * kLn2);
-          }
+          for (int e = 0; e < G; ++e) pbar += Pb[(qr * G + e) * kBlock + key];
+          pbar *= 1.0f / G;
+          dz[vv] = lam * (ppx - pbar);
+          if (EXTRA && kl != nullptr && pbar > 0.f) klv = pbar * (logf(pbar) - lz * kLn2);
+          if (EXTRA && dscore != nullptr)
+            dscore[((((size_t)b * N + tqq) * H_kv + g) * topk + qry_slot[qr]) * kBlock + key] = dz[vv];
         }
       }
+      if (EXTRA && kl != nullptr) {
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) klv += __shfl_xor(klv, off);   // over the half-wave's 32 keys
+        if (n == 0 && qr < TQ) atomicAdd(&qry_kl[qr], klv);
+      }
+    }
     {
-      f4 zs0, zs1;
+      f32x16 zs;
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        zs0[vv] = dz[0][vv] * scale_idx;
-        zs1[vv] = dz[1][vv] * scale_idx;
+      for (int vv = 0; vv < 16; ++vv) zs[vv] = dz[vv] * scale_idx;
+#pragma unroll
+      for (int kc = 0; kc < KCQ; ++kc) {
+        const bf16x8 zb = cfrag(zs, kc);
+#pragma unroll
+        for (int dt = 0; dt < DTI; ++dt) acc_dki[dt] = mma32(trfrag(QIs, C::PQI, 32 * dt, kc, lane), zb, acc_dki[dt]);
       }
-      const bf16x8 zb = cfrag16(zs0, zs1);
 #pragma unroll
-      for (int dt = 0; dt < DTI; ++dt) acc_dki[dt] = mma16(tfrag16(QIt, C::PR, 16 * dt + nn, lane), zb, acc_dki[dt]);
-#pragma unroll
-      for (int mt = 0; mt < MQ; ++mt)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          const int qr = 16 * mt + 4 * qg + vv;
-          if (qr < TQ) dZs[qr * C::PKT + key] = (bf16)(mt == 0 ? zs0[vv] : zs1[vv]);
-        }
-    }
-    if (dscore != nullptr) {
-#pragma unroll
-      for (int mt = 0; mt < MQ; ++mt)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          const int qr = 16 * mt + 4 * qg + vv;
-          if (qr < TQ && qry_t[qr] >= 0)
-            dscore[((((size_t)b * N + qry_t[qr]) * H_kv + g) * topk + qry_slot[qr]) * kBlock + key] = dz[mt][vv];
-        }
-    }
-    if (kl != nullptr) {
-#pragma unroll
-      for (int mt = 0; mt < MQ; ++mt)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          float x = klv[mt][vv];
-#pragma unroll
-          for (int off = 8; off > 0; off >>= 1) x += __shfl_xor(x, off);   // over the 16 keys of the group
-          const int qr = 16 * mt + 4 * qg + vv;
-          if (nn == 0 && qr < TQ) atomicAdd(&qry_kl[qr], x);
-        }
+      for (int vv = 0; vv < NVQ; ++vv) {
+        const int qr = c_row(vv, lane);
+        if (qr < TQ) dZs[qr * C::PKT + key] = (bf16)zs[vv];
+      }
     }
     __syncthreads();   // dz and the KL partials complete
 
-    // (e) dQ = dS K and dq_idx = dz K_idx: 16x16 output tiles over the waves;
-    // lane = output column, slots = rows 4 qg + v of the tile.
-    for (int tile = wave; tile < NT; tile += kBwdWaves) {
-      const bool is_q = tile < NT_Q;
-      const int rt = is_q ? tile / DT : (tile - NT_Q) / DTI;
-      const int ct = is_q ? tile % DT : (tile - NT_Q) % DTI;
-      const bf16* A = (is_q ? dSs : dZs) + (16 * rt + nn) * C::PKT + 8 * qg;
-      const bf16* Bt = (is_q ? Kt : KIt) + (16 * ct + nn) * C::PKT + 8 * qg;
-      f4 o = zero4();
+    // (e) dQ[rows, wave's 32 columns] = dS K and dq_idx[queries, tile] = dz K_idx
+    // (this wave's share of the keys): lane = output column, slots = rows, so
+    // each atomic instruction covers 32 consecutive floats of one row per
+    // half-wave.  A row without a query adds 0 at the step's first row (always
+    // a real one) instead of branching: the number of atomics per step stays
+    // fixed and the loads of the next step can be waited for alone.
+    if (has_q) {
+      f32x16 o = zero16();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        o = mma16(*reinterpret_cast<const bf16x8*>(A + 32 * kk), *reinterpret_cast<const bf16x8*>(Bt + 32 * kk), o);
+      for (int kc = 0; kc < 8; ++kc)
+        o = mma32(*reinterpret_cast<const bf16x8*>(dSs + n * C::PKT + 16 * kc + 8 * hf), ktf[kc], o);
+      const size_t row0 = ((size_t)b * N + row_t[0]) * H_q + g * G;
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int r = 16 * rt + 4 * qg + vv;
-        if (is_q) {
-          const int tr = row_t[r];
-          if (tr >= 0) atomicAdd(&dq_acc[(((size_t)b * N + tr) * H_q + row_h[r]) * D + 16 * ct + nn], o[vv]);
-        } else if (r < TQ && qry_t[r] >= 0) {
-          atomicAdd(&dq_idx[(((size_t)b * N + qry_t[r]) * H_kv + g) * DIDX + 16 * ct + nn], o[vv]);
-        }
+      for (int vv = 0; vv < 16; ++vv) {
+        const int r = c_row(vv, lane);
+        const int tr = row_t[r];
+        const size_t row = tr >= 0 ? ((size_t)b * N + tr) * H_q + g * G + r % G : row0;
+        atomicAdd(dq_acc + row * D + qcol, tr >= 0 ? o[vv] : 0.f);
       }
     }
-    if (kl != nullptr && threadIdx.x < TQ && qry_t[threadIdx.x] >= 0)
+    {
+      f32x16 o = zero16();
+#pragma unroll
+      for (int kc = 0; kc < KCW; ++kc) {
+        const int k0 = 16 * (kpart * KCW + kc) + 8 * hf;
+        o = mma32(*reinterpret_cast<const bf16x8*>(dZs + n * C::PKT + k0),
+                  *reinterpret_cast<const bf16x8*>(KIt + (32 * itile + n) * C::PKT + k0), o);
+      }
+      const size_t qrow0 = ((size_t)b * N + qry_t[0]) * H_kv + g;
+#pragma unroll
+      for (int vv = 0; vv < NVQ; ++vv) {
+        const int qr = c_row(vv, lane);
+        const int tq = qr < TQ ? qry_t[qr] : -1;
+        const size_t row = tq >= 0 ? ((size_t)b * N + tq) * H_kv + g : qrow0;
+        atomicAdd(dq_idx + row * DIDX + 32 * itile + n, tq >= 0 ? o[vv] : 0.f);
+      }
+    }
+    if (EXTRA && kl != nullptr && threadIdx.x < TQ && qry_t[threadIdx.x] >= 0)
       atomicAdd(&kl[((size_t)b * N + qry_t[threadIdx.x]) * H_kv + g], qry_kl[threadIdx.x]);
+    // Step st + 1's tiles: nothing reads Qs / dOs / QIs or the other table set
+    // after the barrier that closed (d), so this can overlap the atomics.
+    store_step(st + 1);
   }
 
-  // The block's dK, dV (group g) and dk_idx (shared by the groups): lane =
-  // key, slots = d 16 dt + 4 qg + v.
+  // Flush the block's dK, dV (group g) and dk_idx (shared by the groups)
+  // through LDS, so that each atomic instruction covers two 32-float runs of
+  // one key row instead of 32 rows.
+  float* scr = reinterpret_cast<float*>(smem + C::OFF_DS) + wave * 32 * 33;
+  auto flush = [&](const f32x16& acc, float* dst_row0, size_t row_stride) {
+    __syncthreads();
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+    for (int vv = 0; vv < 16; ++vv) scr[n * 33 + c_row(vv, lane)] = acc[vv];
+    __syncthreads();
 #pragma unroll
-    for (int vv = 0; vv < 4; ++vv) {
-      const int dcol = 16 * dt + 4 * qg + vv;
-      atomicAdd(&dk_acc[kv_row * D + dcol], acc_dk[dt][vv]);
-      atomicAdd(&dv_acc[kv_row * D + dcol], acc_dv[dt][vv]);
+    for (int kk = 0; kk < 16; ++kk) {
+      const int kr = 2 * kk + hf;                      // key row of the wave
+      atomicAdd(dst_row0 + (size_t)kr * row_stride + n, scr[kr * 33 + n]);
     }
+  };
+  const size_t kv0 = ((size_t)b * N + (size_t)j * kBlock + 32 * wave) * H_kv + g;   // wave's first key row
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    flush(acc_dk[dt], dk_acc + kv0 * D + 32 * dt, (size_t)H_kv * D);
+    flush(acc_dv[dt], dv_acc + kv0 * D + 32 * dt, (size_t)H_kv * D);
+  }
 #pragma unroll
   for (int dt = 0; dt < DTI; ++dt)
-#pragma unroll
-    for (int vv = 0; vv < 4; ++vv)
-      atomicAdd(&dk_idx[((size_t)b * N + u) * DIDX + 16 * dt + 4 * qg + vv], acc_dki[dt][vv]);
+    flush(acc_dki[dt], dk_idx + ((size_t)b * N + (size_t)j * kBlock + 32 * wave) * DIDX + 32 * dt, (size_t)DIDX);
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst,
@@ -589,7 +717,10 @@ template <int D, int DIDX, int G>
 hipError_t run_main(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w, int grid,
                     hipStream_t s) {
   using C = BwdCfg<D, DIDX>;
-  auto kern = bwd_main_kernel<D, DIDX, G>;
+  // The optional per-score outputs get their own instantiation so that the
+  // plain training path carries none of their registers.
+  auto kern = (a.dscore != nullptr || a.kl != nullptr) ? bwd_main_kernel<D, DIDX, G, true>
+                                                       : bwd_main_kernel<D, DIDX, G, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
   if (e != hipSuccess) return e;
@@ -670,13 +801,12 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   prof_end(s);
-  // Work items over the whole sequence.
+  // Index log-sum-exp over the selected support (items of <= 128 queries).
   if ((e = launch_block_items(P, m, 0, P.N, kItemQueries, s)) != hipSuccess) return e;
   size_t grid = block_items_upper_bound(P, 0, P.N, kItemQueries);
   grid = (grid + 7) & ~size_t(7);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int n_lists = P.B * P.H_kv * P.nblk;
-  // Index log-sum-exp over the selected support.
   prof_begin("bwd_idx_lse", s);
   if (P.d_idx == 64)
     hipLaunchKernelGGL(idx_lse_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16*>(a.q_idx),
@@ -686,11 +816,15 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
     hipLaunchKernelGGL(idx_lse_kernel<32>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16*>(a.q_idx),
                        static_cast<const bf16*>(a.k_idx), a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.idx_part,
                        P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, n_lists, P.scale_idx, (int)(grid / 8));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(idx_lse_merge_kernel, dim3((unsigned)((rows_g + 255) / 256)), dim3(256), 0, s, w.idx_part,
                      a.block_idx, w.lse_idx, rows_g, P.topk);
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // Long items (own queries + up to kBigItem list entries) for the main kernel.
+  if ((e = launch_block_items(P, m, 0, P.N, kBigItem, s, 1)) != hipSuccess) return e;
+  grid = block_items_upper_bound(P, 0, P.N, kBigItem);
+  grid = (grid + 7) & ~size_t(7);
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   // Fused main + index backward.
   prof_begin("bwd_main", s);
   if (P.d == 128 && P.d_idx == 64) e = run_main_g<128, 64>(P, a, m, w, (int)grid, s);
