@@ -70,6 +70,18 @@ def algorithmic_work(w) -> dict:
     return out
 
 
+# Symbol of each kernel in the library (for matching counter records).
+KERNEL_SYMBOL = {
+    "index_topk": "index_topk_kernel",
+    "fwd_partial": "sparse_fwd_kernel",
+    "fwd_merge": "fwd_merge_kernel",
+    "bwd_main": "bwd_main_kernel",
+    "bwd_idx_lse": "idx_lse_kernel",
+}
+# The calibration copy: torch.neg over fp32, one read and one write of the buffer.
+COPY_SYMBOL = "neg_kernel"
+
+
 def source_sha(kernel: str) -> str | None:
     f = KERNEL_SOURCE.get(kernel)
     if f is None:
@@ -88,6 +100,44 @@ def measured_traffic(kernel: str, workload: str):
     if rec.get("source_sha256") != source_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _counter_per_dispatch(csv_path: str, symbol: str, counter: str) -> list[float]:
+    """Values of `counter` (summed over its instances) per dispatch of the
+    kernels whose name contains `symbol`, from a rocprofv3 counter CSV."""
+    import csv
+    per = {}
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            if symbol in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def write_traffic(kernel: str, workload: str, fetch_csv: str, write_csv: str, copy_mib: int, command: str):
+    """HBM bytes per launch of `kernel` from two counter runs (FETCH_SIZE, then
+    WRITE_SIZE, both in KiB per dispatch), each scaled by the ratio of the known
+    bytes of the calibration copy to what the same counter read for it."""
+    sym = KERNEL_SYMBOL[kernel]
+    copy_bytes = copy_mib * 2.0 ** 20
+    out = {"kernel": kernel, "workload": workload, "source_sha256": source_sha(kernel), "command": command,
+           "copy_bytes": copy_bytes}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = _counter_per_dispatch(path, sym, counter)
+        cal = _counter_per_dispatch(path, COPY_SYMBOL, counter)
+        if not vals or not cal:
+            raise SystemExit(f"{path}: no {counter} records for {sym} or the calibration copy")
+        kib = float(np.mean(vals))
+        factor = copy_bytes / (float(np.median(cal)) * 1024.0)
+        out[counter] = {"kib_per_dispatch": kib, "dispatches": len(vals), "copy_kib": float(np.median(cal)),
+                        "factor": factor, "bytes": kib * 1024.0 * factor}
+        total += kib * 1024.0 * factor
+    out["bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def cpu_baseline(w, x, rows_n: int, seed: int = 0) -> dict | None:
@@ -136,7 +186,20 @@ def main() -> int:
     ap.add_argument("--workload", default="fwdbwd-bf16-n128k")
     ap.add_argument("--variant", default="normal", choices=["normal", "int", "planted"])
     ap.add_argument("--cpu-rows", type=int, default=512, help="query rows for the oracle baseline (0: skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, run a plain fp32 copy (torch.neg) of this many MiB three times: "
+                         "the known-size kernel that calibrates the HBM byte counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 counter CSVs (FETCH_SIZE, WRITE_SIZE) of this workload, "
+                         "taken with --copy-mib, into profiles/traffic_<kernel>_<workload>.json")
+    ap.add_argument("--traffic-kernel", default="bwd_main")
+    ap.add_argument("--traffic-command", default="", help="the rocprofv3 command the CSVs came from (recorded)")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        write_traffic(args.traffic_kernel, args.workload, *args.traffic_from, args.copy_mib or 1024,
+                      args.traffic_command)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -177,6 +240,13 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     prof = msa.profile_collect()
     msa.profile_enable(False)
+    if args.copy_mib > 0:
+        src = torch.randn(args.copy_mib * 2 ** 18, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = w.B * w.N * args.steps / elapsed
