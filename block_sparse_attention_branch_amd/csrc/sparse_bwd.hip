@@ -20,8 +20,8 @@
 //   idx_lse_kernel       per (KV block, selecting queries): log-sum-exp of
 //                        the index logits over the block (KV-outer, MFMA)
 //   idx_lse_merge_kernel lse_idx[b,t,g] over the selected support
-//   bwd_main_kernel      per work item (KV block j of group g, <= 128 queries
-//                        that selected it): 4 waves, wave w owns keys
+//   bwd_main_kernel      per work item (KV block j of group g, <= 1024 + 128
+//                        queries that selected it): 4 waves, wave w owns keys
 //                        32w..32w+31 and keeps dK, dV, dk_idx of those keys in
 //                        registers; per 32 (query, head) rows it rebuilds
 //                        S = Q K^T and P, dP = dO V^T, dS = P (dP - D), the
@@ -70,10 +70,9 @@ struct Item {
 
 __device__ inline bool decode_item(const int32_t* __restrict__ tiles, const int32_t* __restrict__ pos,
                                    const int32_t* __restrict__ offs, const int32_t* __restrict__ rows,
-                                   int n_lists, int per_xcd, int N, int H_kv, int topk, int nblk, int nsb,
-                                   Item* it) {
-  const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (w >= tiles[n_lists]) return false;
+                                   int n_lists, int N, int H_kv, int topk, int nblk, int nsb, Item* it) {
+  const int w = xcd_item(tiles[n_lists]);
+  if (w < 0) return false;
   int lo = 0, hi = n_lists - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -130,12 +129,12 @@ __global__ __launch_bounds__(256) void idx_lse_kernel(
     const bf16* __restrict__ q_idx, const bf16* __restrict__ k_idx, const int32_t* __restrict__ block_idx,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ offs, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ tiles, float2* __restrict__ part, int N, int H_kv, int topk, int causal,
-    int nblk, int nsb, int n_lists, float scale_idx, int per_xcd) {
+    int nblk, int nsb, int n_lists, float scale_idx) {
   constexpr int PK = DIDX + 8;
   constexpr int KSTEPS = DIDX / 16;
   __shared__ __align__(16) bf16 Ks[kBlock * PK];
   Item it;
-  if (!decode_item(tiles, pos, offs, rows, n_lists, per_xcd, N, H_kv, topk, nblk, nsb, &it)) return;
+  if (!decode_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, &it)) return;
   {
     const bf16* src = k_idx + ((size_t)it.b * N + (size_t)it.j * kBlock) * DIDX;
     constexpr int CPR = DIDX / 8;
@@ -254,10 +253,9 @@ struct BigItem {
 
 __device__ inline bool decode_big_item(const int32_t* __restrict__ tiles, const int32_t* __restrict__ pos,
                                        const int32_t* __restrict__ offs, const int32_t* __restrict__ rows,
-                                       int n_lists, int per_xcd, int N, int H_kv, int topk, int nblk, int nsb,
-                                       BigItem* it) {
-  const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (w >= tiles[n_lists]) return false;
+                                       int n_lists, int N, int H_kv, int topk, int nblk, int nsb, BigItem* it) {
+  const int w = xcd_item(tiles[n_lists]);
+  if (w < 0) return false;
   int lo = 0, hi = n_lists - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -334,13 +332,6 @@ __device__ inline bf16x8 cfrag(const f32x16& x, int kc) {
 __device__ inline f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-// Add a C-layout column (lane = output row, slots = 16 consecutive-by-group
-// columns 8 (v/4) + v%4 past `base`, which already includes 4 (l/32)).
-__device__ inline void atomic_add_col(float* base, const f32x16& x) {
-#pragma unroll
-  for (int vv = 0; vv < 16; ++vv) atomicAdd(base + 8 * (vv >> 2) + (vv & 3), x[vv]);
-}
-
 template <int D, int DIDX, int G, bool EXTRA>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -350,7 +341,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     const int32_t* __restrict__ rows, const int32_t* __restrict__ tiles, float* __restrict__ dq_acc,
     float* __restrict__ dk_acc, float* __restrict__ dv_acc, float* __restrict__ dq_idx,
     float* __restrict__ dk_idx, float* __restrict__ dscore, float* __restrict__ kl, int N, int H_kv, int topk,
-    int causal, int nblk, int nsb, int n_lists, float scale, float scale_idx, float lam, int per_xcd) {
+    int causal, int nblk, int nsb, int n_lists, float scale, float scale_idx, float lam) {
   using C = BwdCfg<D, DIDX>;
   constexpr int KS = D / 16;        // 16-wide k-steps over d
   constexpr int KSI = DIDX / 16;    // 16-wide k-steps over d_idx
@@ -376,7 +367,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   bf16* KIt = reinterpret_cast<bf16*>(smem + C::OFF_KIT);
 
   BigItem it;
-  if (!decode_big_item(tiles, pos, offs, rows, n_lists, per_xcd, N, H_kv, topk, nblk, nsb, &it)) return;
+  if (!decode_big_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, &it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, hf = lane >> 5;
   const int H_q = H_kv * G;
@@ -729,7 +720,7 @@ hipError_t run_main(const Problem& P, const BwdArgs& a, const BlockMap& m, const
                      a.lse, w.D, static_cast<const bf16*>(a.q_idx), static_cast<const bf16*>(a.k_idx), w.lse_idx,
                      a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.dq_acc, w.dk_acc, w.dv_acc, a.dq_idx,
                      a.dk_idx, a.dscore, a.kl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb,
-                     P.B * P.H_kv * P.nblk, P.scale, P.scale_idx, a.kl_weight, grid / 8);
+                     P.B * P.H_kv * P.nblk, P.scale, P.scale_idx, a.kl_weight);
   return hipGetLastError();
 }
 
@@ -811,11 +802,11 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
   if (P.d_idx == 64)
     hipLaunchKernelGGL(idx_lse_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16*>(a.q_idx),
                        static_cast<const bf16*>(a.k_idx), a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.idx_part,
-                       P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, n_lists, P.scale_idx, (int)(grid / 8));
+                       P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, n_lists, P.scale_idx);
   else
     hipLaunchKernelGGL(idx_lse_kernel<32>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16*>(a.q_idx),
                        static_cast<const bf16*>(a.k_idx), a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.idx_part,
-                       P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, n_lists, P.scale_idx, (int)(grid / 8));
+                       P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, n_lists, P.scale_idx);
   hipLaunchKernelGGL(idx_lse_merge_kernel, dim3((unsigned)((rows_g + 255) / 256)), dim3(256), 0, s, w.idx_part,
                      a.block_idx, w.lse_idx, rows_g, P.topk);
   prof_end(s);

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ rows, const int32_t* __restrict__ tiles,
     T* __restrict__ po, float* __restrict__ plse, int N, int H_kv, int topk, int causal, int nblk,
-    int nsb, int s_lo, int s_hi, int c0, int c1, int n_lists, float scale, int per_xcd) {
+    int nsb, int s_lo, int s_hi, int c0, int c1, int n_lists, float scale) {
   using C = FwdCfg<T, D>;
   using M = Mma<T>;
   constexpr int KPL = C::KPL;
@@ -110,9 +110,8 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
   const int H_q = H_kv * G;
   const int CQ = c1 - c0;
 
-  // Work item of this workgroup (XCD-contiguous numbering).
-  const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (w >= tiles[n_lists]) return;
+  const int w = xcd_item(tiles[n_lists]);
+  if (w < 0) return;
   int lo = 0, hi = n_lists - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -323,7 +322,7 @@ hipError_t run_fwd(const Problem& P, const T* q, const T* k, const T* v, const i
     prof_begin("fwd_partial", s);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kFwdThreads), C::LDS, s, q, k, v, block_idx, m.pos,
                        m.offs, m.rows, m.tiles, po, pl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, s_lo,
-                       s_hi, c0, c1, n_lists, P.scale, (int)(grid / 8));
+                       s_hi, c0, c1, n_lists, P.scale);
     prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     constexpr int LPR = D / (16 / (int)sizeof(T));
