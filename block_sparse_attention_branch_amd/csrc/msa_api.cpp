@@ -308,6 +308,8 @@ MSA_API int msa_sparse_bwd(const msa_dims* dims, const void* q, const void* k, c
   REQUIRE(dk_idx);
   if (!std::isfinite(kl_weight)) return fail(MSA_ERR_INVALID_ARG, "kl_weight must be finite");
   if (P.dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_bwd supports bf16 only");
+  if ((size_t)P.B * P.N * P.H_q >= (size_t(1) << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_bwd needs B * N * H_q < 2^31 (query rows are indexed in 32 bits)");
   const size_t map_bytes = align_up(msa::block_map_bytes(P));
   st = check_ws(workspace, workspace_bytes, map_bytes + align_up(msa::sparse_bwd_scratch_bytes(P)));
   if (st != MSA_OK) return st;

@@ -224,23 +224,39 @@ constexpr int kMainThreads = kBwdWaves * kWave;
 // per-item flush of dK, dV and dk_idx rare.
 constexpr int kBigItem = 1024;
 
+// Per-step tables (32 entries each) in LDS, double buffered.
+enum : int {
+  kRowT = 0,     // t of the row, -1 past the item's end
+  kRowCut,       // key u is visible to the row iff u <= cut (-1: none)
+  kRowLse,       // LSE * log2(e)
+  kRowD,         // rowsum(dO * O)
+  kRowId,        // (b N + t) H_q + h, or -1
+  kQryT,         // per query of the step: t or -1
+  kQrySlot,      // position of block j in the query's selection
+  kQryCut,       // visibility cut-off of the query (-1: none)
+  kQryLse,       // index LSE * log2(e)
+  kQryKl,        // KL partial (optional output)
+  kQryId,        // (b N + t) H_kv + g, or -1
+  kNumTabs
+};
+
 template <int D, int DIDX>
 struct BwdCfg {
-  static constexpr int PKT = kBlock + 8;   // rows of 128 keys (+16 B)
+  static constexpr int PKT = kBlock + 8;   // K_idx^T rows of 128 keys (+16 B)
   static constexpr int PQ = D + 8;         // Q / dO rows (+16 B)
   static constexpr int PQI = DIDX + 8;     // q_idx rows (+16 B)
-  static constexpr size_t OFF_QS = 0;                                   // Q        [32][PQ]
-  static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;       // dO       [32][PQ]
-  static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;      // q_idx    [32][PQI]
-  static constexpr size_t OFF_DS = OFF_QIS + (size_t)32 * PQI * 2;      // dS       [32][PKT]
-  static constexpr size_t OFF_DZ = OFF_DS + (size_t)32 * PKT * 2;       // dz       [32][PKT]
-  static constexpr size_t OFF_PB = OFF_DZ + (size_t)32 * PKT * 2;       // P        [32][128] fp32
-  static constexpr size_t OFF_TAB = OFF_PB + (size_t)32 * kBlock * 4;   // 2 x 10 x [32] step tables
-  static constexpr size_t OFF_KIT = OFF_TAB + 2 * 10 * 32 * 4;          // K_idx^T  [DIDX][PKT]
-  static constexpr size_t OFF_QL = OFF_KIT + (size_t)DIDX * PKT * 2;    // item queries: (t << 6) | slot
+  static constexpr int PST = 32 + 4;       // dS^T / dz^T: one row of 32 step rows per key (+8 B)
+  static constexpr size_t OFF_QS = 0;                                    // Q        [32][PQ]
+  static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;        // dO       [32][PQ]
+  static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;       // q_idx    [32][PQI]
+  static constexpr size_t OFF_DST = OFF_QIS + (size_t)32 * PQI * 2;      // dS^T     [128][PST]
+  static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     [128][PST]
+  static constexpr size_t OFF_TAB = OFF_DZT + (size_t)kBlock * PST * 2;  // 2 x kNumTabs x [32]
+  static constexpr size_t OFF_KIT = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K_idx^T [DIDX][PKT]
+  static constexpr size_t OFF_QL = OFF_KIT + (size_t)DIDX * PKT * 2;     // item queries: (t << 6) | slot
   static constexpr size_t LDS = OFF_QL + (size_t)(kBlock + kBigItem) * 4;
-  // The flush at the end of an item reuses [OFF_DS, OFF_TAB) as 4 x [32][33] fp32.
-  static_assert(OFF_TAB - OFF_DS >= 4 * 32 * 33 * 4, "flush scratch");
+  // The flush at the end of an item reuses [OFF_QS, OFF_TAB) as 4 x [32][33] fp32.
+  static_assert(OFF_TAB - OFF_QS >= 4 * 32 * 33 * 4, "flush scratch");
 };
 
 // A work item of the main kernel and the queries it covers: item-local query
@@ -274,15 +290,13 @@ __device__ inline bool decode_big_item(const int32_t* __restrict__ tiles, const 
   return true;
 }
 
-// t (-1 when qi is past the item), visibility cut-off (key u is visible iff
-// u <= cut) and, when asked, the slot of block j in the query's row.
+// t (-1 when qi is past the item) and, when asked, the slot of block j in the
+// query's row.
 __device__ inline int big_query(const BigItem& it, int qi, const int32_t* __restrict__ block_idx, int N, int H_kv,
-                                int topk, int causal, bool want_slot, int* cut, int* slot) {
+                                int topk, bool want_slot, int* slot) {
   *slot = 0;
-  *cut = -1;
   if (qi < it.n_own) {
     const int t = it.j * kBlock + qi;
-    *cut = causal ? t : 0x7fffffff;
     if (want_slot) {
       const int32_t* brow = block_idx + (((size_t)it.b * N + t) * H_kv + it.g) * topk;
       for (int e = 0; e < topk; ++e)
@@ -296,7 +310,6 @@ __device__ inline int big_query(const BigItem& it, int qi, const int32_t* __rest
   const int t = e >> 6;
   if (t < 0 || t >= N || (e & 63) >= topk) return -1;   // malformed map: drop the entry
   *slot = e & 63;
-  *cut = 0x7fffffff;
   return t;
 }
 
@@ -322,6 +335,15 @@ __device__ inline bf16x8 trfrag(const bf16* base, int pitch, int m0, int kc, int
   r[4] = h4[0]; r[5] = h4[1]; r[6] = h4[2]; r[7] = h4[3];
   return r;
 }
+// Key of K slot i of half-wave hf in 16-key chunk kc, in the order trfrag
+// delivers it (see above).
+__device__ inline int tr_key(int kc, int hf, int i) { return 16 * kc + 4 * hf + (i & 3) + 8 * (i >> 2); }
+// Position that key kk takes in a row stored so that a plain 16-byte read at
+// 16 kc + 8 hf yields the keys tr_key(kc, hf, 0..7).
+__device__ inline int tr_pos(int kk) {
+  const int r = kk & 15;
+  return (kk & ~15) + 8 * ((r >> 2) & 1) + (r & 3) + 4 * (r >> 3);
+}
 // Matching B operand: slots 8kc .. 8kc+7 of a C-layout tile.
 __device__ inline bf16x8 cfrag(const f32x16& x, int kc) {
   bf16x8 r;
@@ -332,6 +354,82 @@ __device__ inline bf16x8 cfrag(const f32x16& x, int kc) {
 __device__ inline f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ inline bf16x4 pack4(float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (bf16)a; r[1] = (bf16)b; r[2] = (bf16)c; r[3] = (bf16)d;
+  return r;
+}
+// x of lane l % 32 (lo) and of lane l % 32 + 32 (hi), in every lane.
+__device__ inline void halves(float x, float* lo, float* hi) {
+  const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  *lo = __uint_as_float(v[0]);
+  *hi = __uint_as_float(v[1]);
+}
+
+// Mean over the G heads of each query of a 32-row C-layout tile whose row
+// q G + e is head e of query q, returned in the C layout of a tile whose rows
+// are the queries (slot v of half hf holds query c_row(v, hf)); slots that hold
+// no query of the step are left 0.
+template <int G>
+__device__ inline f32x16 head_mean(const f32x16& p, int hf) {
+  f32x16 r = zero16();
+  constexpr float inv = 1.0f / G;
+  if constexpr (G == 1) {
+    r = p;
+  } else if constexpr (G >= 8) {
+    // rows qG .. qG+G-1: slots [q G/2, (q+1) G/2) of both halves
+    constexpr int H2 = G / 2;
+#pragma unroll
+    for (int q = 0; q < 32 / G; ++q) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < H2; ++e) s += p[q * H2 + e];
+      float lo, hi;
+      halves(s, &lo, &hi);
+      r[q] = (lo + hi) * inv;
+    }
+  } else if constexpr (G == 4) {
+    // slots 4gi .. 4gi+3 of half h: query 2gi + h
+    float x0[4], x1[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) halves(p[4 * gi] + p[4 * gi + 1] + p[4 * gi + 2] + p[4 * gi + 3], &x0[gi], &x1[gi]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {   // query 4 hf + v
+      const float* x = (v & 1) ? x1 : x0;
+      r[v] = (hf ? x[2 + (v >> 1)] : x[v >> 1]) * inv;
+    }
+  } else {
+    static_assert(G == 2, "group size");
+    // slots 4gi + 2k, 4gi + 2k + 1 of half h: query 4gi + 2h + k
+    float y0[4][2], y1[4][2];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        halves(p[4 * gi + 2 * k2] + p[4 * gi + 2 * k2 + 1], &y0[gi][k2], &y1[gi][k2]);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {   // query 8 (v / 4) + 4 hf + v % 4
+      const int g0 = 2 * (v >> 2);
+      const float a = ((v >> 1) & 1) ? y1[g0][v & 1] : y0[g0][v & 1];
+      const float c = ((v >> 1) & 1) ? y1[g0 + 1][v & 1] : y0[g0 + 1][v & 1];
+      r[v] = (hf ? c : a) * inv;
+    }
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Main fused backward.  4 waves; wave w owns keys 32w..32w+31 of the block.
+// 32x32x16 MFMA tiles (C-layout: lane l holds column l % 32, rows
+// 8*(v/4) + 4*(l/32) + v%4 in slot v; A/B operands: lane l holds row/column
+// l % 32 and k = 8*(l/32) + i).  Per step of 32 (query, head) rows:
+//   S = Q K_w^T, dP = dO V_w^T, r = q_idx K_idx,w^T  (A from LDS, B in registers)
+//   P, dS; the head-mean teacher pbar, p_px and dz    (lane = key, all in registers)
+//   dV_w^T += dO^T P, dK_w^T += Q^T dS, dk_idx_w^T += q_idx^T dz
+//   dS^T, dz^T -> LDS; barrier
+//   dQ[:, 32w..32w+31] = dS K and dq_idx = dz K_idx  (A by transpose reads of dS^T /
+//                                        dz^T, B = K^T / K_idx^T in the matching key order)
+// ---------------------------------------------------------------------------
 template <int D, int DIDX, int G, bool EXTRA>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -353,6 +451,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   constexpr int CPR = D / 8;        // 16-byte chunks per Q / dO row
   constexpr int CPRI = DIDX / 8;    // 16-byte chunks per q_idx row
   constexpr int LDM = 32 * CPR / kMainThreads;              // Q (and dO) chunks per thread
+  constexpr int NT = kNumTabs * 32;
   static_assert(32 * CPR % kMainThreads == 0, "tile split");
   static_assert(32 * CPRI <= kMainThreads, "q_idx tile split");
   static_assert(DT <= kBwdWaves, "one dQ column tile per wave");
@@ -360,11 +459,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   bf16* Qs = reinterpret_cast<bf16*>(smem + C::OFF_QS);
   bf16* dOs = reinterpret_cast<bf16*>(smem + C::OFF_DOS);
   bf16* QIs = reinterpret_cast<bf16*>(smem + C::OFF_QIS);
-  bf16* dSs = reinterpret_cast<bf16*>(smem + C::OFF_DS);
-  bf16* dZs = reinterpret_cast<bf16*>(smem + C::OFF_DZ);
-  float* Pb = reinterpret_cast<float*>(smem + C::OFF_PB);
-  int* tabs = reinterpret_cast<int*>(smem + C::OFF_TAB);        // [2][10][32]
+  bf16* dSt = reinterpret_cast<bf16*>(smem + C::OFF_DST);
+  bf16* dZt = reinterpret_cast<bf16*>(smem + C::OFF_DZT);
+  int* tabs = reinterpret_cast<int*>(smem + C::OFF_TAB);
   bf16* KIt = reinterpret_cast<bf16*>(smem + C::OFF_KIT);
+  int* qlist = reinterpret_cast<int*>(smem + C::OFF_QL);   // (t << 6) | slot, or -1
 
   BigItem it;
   if (!decode_big_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, &it)) return;
@@ -378,26 +477,27 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   const size_t blk_row0 = ((size_t)b * N + (size_t)j * kBlock) * H_kv + g;   // key 0 of the block
   const int nq = it.n_own + it.ne;
   const bool want_slot = EXTRA && dscore != nullptr;
-  int* qlist = reinterpret_cast<int*>(smem + C::OFF_QL);   // (t << 6) | slot, or -1
 
   // The item's queries in LDS, so that the step loop needs no dependent
   // global load (the vector-memory counter is in order: a wait on a
   // dependent load would also wait for the previous step's atomics).
   for (int qi = threadIdx.x; qi < nq; qi += kMainThreads) {
-    int cut, slot;
-    const int t = big_query(it, qi, block_idx, N, H_kv, topk, causal, want_slot, &cut, &slot);
+    int slot;
+    const int t = big_query(it, qi, block_idx, N, H_kv, topk, want_slot, &slot);
     qlist[qi] = t < 0 ? -1 : ((t << 6) | slot);
   }
-  // K_idx^T of the block in LDS (B operand of dq_idx).
+  // K_idx^T of the block in LDS (B operand of dq_idx), keys in the order of
+  // the transpose-read A operand.
   for (int c = threadIdx.x; c < kBlock * (DIDX / 8); c += kMainThreads) {
     const int kk = c / (DIDX / 8), col = (c % (DIDX / 8)) * 8;
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
+    const int pk = tr_pos(kk);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) KIt[(col + i) * C::PKT + kk] = x[i];
+    for (int i = 0; i < 8; ++i) KIt[(col + i) * C::PKT + pk] = x[i];
   }
   // Register operands for the whole item: this wave's 32 keys of K, V, K_idx
   // (B of S, dP, r: lane = key, K = d), and K^T of the wave's 32 dQ columns
-  // (B of dQ: lane = column, K = keys).
+  // (B of dQ: lane = column, K = keys in transpose-read order).
   bf16x8 kf[KS], vf[KS], kif[KSI], ktf[8];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -409,18 +509,16 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     kif[ks] = *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + u) * DIDX + 16 * ks + 8 * hf);
   const int qcol = 32 * wave + n;                     // dQ column (wave < DT)
   const bool has_q = DT == kBwdWaves || wave < DT;
-  // dq_idx: output tile wave % DTI, over keys [kpart * KPW, (kpart + 1) * KPW)
-  // of the block, so every wave issues the same atomics.
+  // dq_idx: output tile wave % DTI, over the 16-key chunks
+  // [kpart * KCW, (kpart + 1) * KCW), so every wave issues the same atomics.
   constexpr int KPARTS = kBwdWaves / DTI;
-  constexpr int KCW = 8 / KPARTS;                     // 16-key chunks per wave
+  constexpr int KCW = 8 / KPARTS;
   const int itile = wave % DTI, kpart = wave / DTI;
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kk = 16 * kc + 8 * hf + i;
-      ktf[kc][i] = has_q ? k[(blk_row0 + (size_t)kk * H_kv) * D + qcol] : (bf16)0.f;
-    }
+    for (int i = 0; i < 8; ++i)
+      ktf[kc][i] = has_q ? k[(blk_row0 + (size_t)tr_key(kc, hf, i) * H_kv) * D + qcol] : (bf16)0.f;
 
   f32x16 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
 #pragma unroll
@@ -433,22 +531,26 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   __syncthreads();   // item query list and K_idx^T ready
 
   // Per-thread share of a step, loaded one step ahead into registers: LDM
-  // 16-byte chunks of Q and dO (with LSE, D and the cut-off of rows whose
+  // 16-byte chunks of Q and dO (with LSE, D, cut-off and id of the rows whose
   // first chunk it holds), one chunk of q_idx, and - for threads < TQ - the
-  // step's query table entry (t, slot, cut-off, index LSE).
+  // step's query table entry.  The query-list entries these loads need are
+  // read from LDS one step earlier still (pk_*), so issuing the loads waits
+  // for nothing.
   bf16x8 pre_q[LDM], pre_d[LDM], pre_qi = bf16x8{};
   float pre_lse[LDM], pre_D[LDM], pre_qlse = 0.f;
-  int pre_t[LDM], pre_cut[LDM], pre_qt = -1, pre_qslot = 0, pre_qcut = -1;
+  int pre_t[LDM], pre_cut[LDM], pre_id[LDM], pre_qt = -1, pre_qslot = 0, pre_qcut = -1, pre_qid = -1;
+  int pk_e[LDM], pk_qi = -1, pk_qt = -1;
   const int ld_col = (threadIdx.x % CPR) * 8;
   const int ld_qr = threadIdx.x / CPRI, ld_qcol = (threadIdx.x % CPRI) * 8;
   const bool ld_idx = threadIdx.x < 32 * CPRI;
-  // Query qi of the item: t (-1 past the end), slot, visibility cut-off.
-  auto query = [&](int qi, int* slot, int* cut) {
-    const int e = qi < nq ? qlist[qi] : -1;
-    const int t = e < 0 ? -1 : (e >> 6);
-    *slot = e < 0 ? 0 : (e & 63);
-    *cut = t < 0 ? -1 : ((qi < it.n_own && causal) ? t : 0x7fffffff);
-    return t;
+  const int tx = threadIdx.x & 31;
+  auto entry = [&](int qi) { return qi < nq ? qlist[qi] : -1; };
+  auto cutoff = [&](int qi, int t) { return t < 0 ? -1 : ((qi < it.n_own && causal) ? t : 0x7fffffff); };
+  auto peek = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < LDM; ++c) pk_e[c] = entry((32 * st + (threadIdx.x + c * kMainThreads) / CPR) / G);
+    pk_qi = ld_qr < TQ ? entry(st * TQ + ld_qr) : -1;
+    pk_qt = tx < TQ ? entry(st * TQ + tx) : -1;
   };
   // Every load below is unconditional (clamped to a valid row) so that the
   // compiler can count them exactly and later wait for them without also
@@ -457,79 +559,77 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
 #pragma unroll
     for (int c = 0; c < LDM; ++c) {
       const int r = (threadIdx.x + c * kMainThreads) / CPR;
-      int slot;
-      pre_t[c] = query((32 * st + r) / G, &slot, &pre_cut[c]);
-      const size_t qrow = ((size_t)b * N + (pre_t[c] < 0 ? 0 : pre_t[c])) * H_q + g * G + r % G;
+      const int t = pk_e[c] < 0 ? -1 : (pk_e[c] >> 6);
+      pre_t[c] = t;
+      pre_cut[c] = cutoff((32 * st + r) / G, t);
+      const size_t qrow = ((size_t)b * N + (t < 0 ? 0 : t)) * H_q + g * G + r % G;
+      pre_id[c] = t < 0 ? -1 : (int)qrow;
       pre_q[c] = *reinterpret_cast<const bf16x8*>(q + qrow * D + ld_col);
       pre_d[c] = *reinterpret_cast<const bf16x8*>(dO + qrow * D + ld_col);
       pre_lse[c] = lse[qrow];
       pre_D[c] = Dv[qrow];
     }
     {
-      int cut, slot;
-      const int qr = ld_qr < 32 ? ld_qr : 31;
-      const int tq = qr < TQ ? query(st * TQ + qr, &slot, &cut) : -1;
+      const int tq = pk_qi < 0 ? -1 : (pk_qi >> 6);
       pre_qi = *reinterpret_cast<const bf16x8*>(q_idx + (((size_t)b * N + (tq < 0 ? 0 : tq)) * H_kv + g) * DIDX +
                                                 ld_qcol);
       if (tq < 0) pre_qi = bf16x8{};
     }
     {
-      const int x = threadIdx.x & 31;
-      pre_qt = x < TQ ? query(st * TQ + x, &pre_qslot, &pre_qcut) : -1;
-      pre_qlse = lse_idx[((size_t)b * N + (pre_qt < 0 ? 0 : pre_qt)) * H_kv + g];
+      pre_qt = pk_qt < 0 ? -1 : (pk_qt >> 6);
+      pre_qslot = pk_qt < 0 ? 0 : (pk_qt & 63);
+      pre_qcut = cutoff(st * TQ + tx, pre_qt);
+      const size_t qrow = ((size_t)b * N + (pre_qt < 0 ? 0 : pre_qt)) * H_kv + g;
+      pre_qid = pre_qt < 0 ? -1 : (int)qrow;
+      pre_qlse = lse_idx[qrow];
     }
   };
-
-  const float c_s = scale * kLog2e;
-  const float c_i = scale_idx * kLog2e;
-  const int n_steps = (nq * G + 31) / 32;
-  // Store a step's prefetched registers into its LDS tiles and step tables
-  // (rows: t or -1, cut-off, LSE * log2(e), D; queries: t or -1, slot,
-  // cut-off, index LSE * log2(e), KL partial).
+  // Store a step's prefetched registers into its LDS tiles and tables.
   auto store_step = [&](int st) {
-    int* tb = tabs + (st & 1) * 320;
+    int* tb = tabs + (st & 1) * NT;
+    float* tf = reinterpret_cast<float*>(tb);
 #pragma unroll
     for (int c = 0; c < LDM; ++c) {
       const int r = (threadIdx.x + c * kMainThreads) / CPR;
       *reinterpret_cast<bf16x8*>(Qs + r * C::PQ + ld_col) = pre_q[c];
       *reinterpret_cast<bf16x8*>(dOs + r * C::PQ + ld_col) = pre_d[c];
       if (ld_col == 0) {
-        tb[r] = pre_t[c];
-        tb[32 + r] = pre_t[c] < 0 ? -1 : pre_cut[c];
-        reinterpret_cast<float*>(tb)[64 + r] = pre_lse[c] * kLog2e;
-        reinterpret_cast<float*>(tb)[96 + r] = pre_D[c];
+        tb[kRowT * 32 + r] = pre_t[c];
+        tb[kRowCut * 32 + r] = pre_cut[c];
+        tf[kRowLse * 32 + r] = pre_lse[c] * kLog2e;
+        tf[kRowD * 32 + r] = pre_D[c];
+        tb[kRowId * 32 + r] = pre_id[c];
       }
     }
     if (ld_idx) *reinterpret_cast<bf16x8*>(QIs + ld_qr * C::PQI + ld_qcol) = pre_qi;
     if (threadIdx.x < 32) {
-      tb[128 + threadIdx.x] = pre_qt;
-      tb[160 + threadIdx.x] = pre_qslot;
-      tb[192 + threadIdx.x] = pre_qt < 0 ? -1 : pre_qcut;
-      reinterpret_cast<float*>(tb)[224 + threadIdx.x] = pre_qlse * kLog2e;
-      reinterpret_cast<float*>(tb)[256 + threadIdx.x] = 0.f;
+      tb[kQryT * 32 + tx] = pre_qt;
+      tb[kQrySlot * 32 + tx] = pre_qslot;
+      tb[kQryCut * 32 + tx] = pre_qcut;
+      tf[kQryLse * 32 + tx] = pre_qlse * kLog2e;
+      tf[kQryKl * 32 + tx] = 0.f;
+      tb[kQryId * 32 + tx] = pre_qid;
     }
   };
+
+  const float c_s = scale * kLog2e;
+  const float c_i = scale_idx * kLog2e;
+  const int n_steps = (nq * G + 31) / 32;
+  peek(0);
   load_step(0);
   store_step(0);
+  peek(1);
 #pragma unroll 1
   for (int st = 0; st < n_steps; ++st) {
     asm volatile("" ::: "memory");
-    int* tb = tabs + (st & 1) * 320;
-    int* row_t = tb;
-    int* row_cut = tb + 32;
-    float* row_lse = reinterpret_cast<float*>(tb + 64);
-    float* row_d = reinterpret_cast<float*>(tb + 96);
-    int* qry_t = tb + 128;
-    int* qry_slot = tb + 160;
-    int* qry_cut = tb + 192;
-    float* qry_lse = reinterpret_cast<float*>(tb + 224);
-    float* qry_kl = reinterpret_cast<float*>(tb + 256);
-    __syncthreads();   // step st's tiles and tables in LDS
+    const int* tb = tabs + (st & 1) * NT;
+    const float* tf = reinterpret_cast<const float*>(tb);
+    __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T / dz^T consumed
     // Prefetch step st + 1 (past the end it re-reads valid rows, unused).
     load_step(st + 1);
+    peek(st + 2);
 
-    // (c) S, dP, index logits (lane = key, slots = rows / queries); P, dS;
-    // dV^T += dO^T P and dK^T += Q^T dS.
+    // S, dP, index logits (lane = key, slots = rows / queries).
     f32x16 s = zero16(), dp = zero16(), ri = zero16();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -539,13 +639,14 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
 #pragma unroll
     for (int ks = 0; ks < KSI; ++ks)
       ri = mma32(*reinterpret_cast<const bf16x8*>(QIs + n * C::PQI + 16 * ks + 8 * hf), kif[ks], ri);
+    // P, dS; dS^T to LDS.
     f32x16 p, ds;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int r4 = 8 * grp + 4 * hf;                 // rows r4 .. r4+3 = slots 4grp .. 4grp+3
-      const int4 cut = *reinterpret_cast<const int4*>(row_cut + r4);
-      const float4 l2 = *reinterpret_cast<const float4*>(row_lse + r4);
-      const float4 dd = *reinterpret_cast<const float4*>(row_d + r4);
+      const int4 cut = *reinterpret_cast<const int4*>(tb + kRowCut * 32 + r4);
+      const float4 l2 = *reinterpret_cast<const float4*>(tf + kRowLse * 32 + r4);
+      const float4 dd = *reinterpret_cast<const float4*>(tf + kRowD * 32 + r4);
       const int cuts[4] = {cut.x, cut.y, cut.z, cut.w};
       const float l2s[4] = {l2.x, l2.y, l2.z, l2.w};
       const float dds[4] = {dd.x, dd.y, dd.z, dd.w};
@@ -555,46 +656,52 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
         const float pv = u <= cuts[e] ? __builtin_amdgcn_exp2f(s[vv] * c_s - l2s[e]) : 0.f;
         p[vv] = pv;
         ds[vv] = pv * (dp[vv] - dds[e]) * scale;
-        Pb[(r4 + e) * kBlock + key] = pv;
-        dSs[(r4 + e) * C::PKT + key] = (bf16)ds[vv];
       }
+      *reinterpret_cast<bf16x4*>(dSt + key * C::PST + r4) =
+          pack4(ds[4 * grp], ds[4 * grp + 1], ds[4 * grp + 2], ds[4 * grp + 3]);
     }
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const bf16x8 pb = cfrag(p, kc), sb = cfrag(ds, kc);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        acc_dv[dt] = mma32(trfrag(dOs, C::PQ, 32 * dt, kc, lane), pb, acc_dv[dt]);
-        acc_dk[dt] = mma32(trfrag(Qs, C::PQ, 32 * dt, kc, lane), sb, acc_dk[dt]);
-      }
-    }
-    __syncthreads();   // P of every head of a query visible to the teacher; dS complete
-
-    // (d) Index branch on the query slots: p_px, teacher pbar, dz.
+    // Index branch on the query slots: teacher pbar (mean of P over the
+    // query's heads), p_px, dz = lam (p_px - pbar); dz^T to LDS.
+    const f32x16 pb = head_mean<G>(p, hf);
     f32x16 dz = zero16();
 #pragma unroll
-    for (int vv = 0; vv < NVQ; ++vv) {
-      const int qr = c_row(vv, lane);
-      float klv = 0.f;
-      if (qr < TQ) {
-        const int tqq = qry_t[qr];
-        if (u <= qry_cut[qr]) {
-          const float lz = ri[vv] * c_i - qry_lse[qr];   // log2 p_px
-          const float ppx = __builtin_amdgcn_exp2f(lz);
-          float pbar = 0.f;
+    for (int gq = 0; gq < NVQ / 4; ++gq) {
+      const int r4 = 8 * gq + 4 * hf;                  // queries r4 .. r4+3 = slots 4gq .. 4gq+3
+      const int4 qc = *reinterpret_cast<const int4*>(tb + kQryCut * 32 + r4);
+      const float4 ql = *reinterpret_cast<const float4*>(tf + kQryLse * 32 + r4);
+      const int qcs[4] = {qc.x, qc.y, qc.z, qc.w};
+      const float qls[4] = {ql.x, ql.y, ql.z, ql.w};
 #pragma unroll
-          for (int e = 0; e < G; ++e) pbar += Pb[(qr * G + e) * kBlock + key];
-          pbar *= 1.0f / G;
-          dz[vv] = lam * (ppx - pbar);
-          if (EXTRA && kl != nullptr && pbar > 0.f) klv = pbar * (logf(pbar) - lz * kLn2);
-          if (EXTRA && dscore != nullptr)
-            dscore[((((size_t)b * N + tqq) * H_kv + g) * topk + qry_slot[qr]) * kBlock + key] = dz[vv];
+      for (int e = 0; e < 4; ++e) {
+        const int vv = 4 * gq + e;
+        const float lz = ri[vv] * c_i - qls[e];       // log2 p_px
+        const bool vis = u <= qcs[e];                  // -1 for rows that hold no query
+        dz[vv] = vis ? lam * (__builtin_amdgcn_exp2f(lz) - pb[vv]) : 0.f;
+        if (EXTRA && dscore != nullptr && vis) {
+          const int qr = r4 + e;
+          dscore[((((size_t)b * N + tb[kQryT * 32 + qr]) * H_kv + g) * topk + tb[kQrySlot * 32 + qr]) * kBlock +
+                 key] = dz[vv];
+        }
+        if (EXTRA && kl != nullptr) {
+          float klv = (vis && pb[vv] > 0.f) ? pb[vv] * (logf(pb[vv]) - lz * kLn2) : 0.f;
+#pragma unroll
+          for (int off = 16; off > 0; off >>= 1) klv += __shfl_xor(klv, off);   // over the half-wave's 32 keys
+          if (n == 0 && r4 + e < TQ) atomicAdd(reinterpret_cast<float*>(tabs + (st & 1) * NT) + kQryKl * 32 + r4 + e, klv);
         }
       }
-      if (EXTRA && kl != nullptr) {
+      if (r4 < TQ)
+        *reinterpret_cast<bf16x4*>(dZt + key * C::PST + r4) =
+            pack4(dz[4 * gq] * scale_idx, dz[4 * gq + 1] * scale_idx, dz[4 * gq + 2] * scale_idx,
+                  dz[4 * gq + 3] * scale_idx);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS, dk_idx^T += q_idx^T dz.
 #pragma unroll
-        for (int off = 16; off > 0; off >>= 1) klv += __shfl_xor(klv, off);   // over the half-wave's 32 keys
-        if (n == 0 && qr < TQ) atomicAdd(&qry_kl[qr], klv);
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 pbf = cfrag(p, kc), sbf = cfrag(ds, kc);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        acc_dv[dt] = mma32(trfrag(dOs, C::PQ, 32 * dt, kc, lane), pbf, acc_dv[dt]);
+        acc_dk[dt] = mma32(trfrag(Qs, C::PQ, 32 * dt, kc, lane), sbf, acc_dk[dt]);
       }
     }
     {
@@ -607,15 +714,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
 #pragma unroll
         for (int dt = 0; dt < DTI; ++dt) acc_dki[dt] = mma32(trfrag(QIs, C::PQI, 32 * dt, kc, lane), zb, acc_dki[dt]);
       }
-#pragma unroll
-      for (int vv = 0; vv < NVQ; ++vv) {
-        const int qr = c_row(vv, lane);
-        if (qr < TQ) dZs[qr * C::PKT + key] = (bf16)zs[vv];
-      }
     }
-    __syncthreads();   // dz and the KL partials complete
+    __syncthreads();   // dS^T, dz^T and the KL partials complete
 
-    // (e) dQ[rows, wave's 32 columns] = dS K and dq_idx[queries, tile] = dz K_idx
+    // dQ[rows, wave's 32 columns] = dS K and dq_idx[queries, tile] = dz K_idx
     // (this wave's share of the keys): lane = output column, slots = rows, so
     // each atomic instruction covers 32 consecutive floats of one row per
     // half-wave.  A row without a query adds 0 at the step's first row (always
@@ -624,45 +726,48 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     if (has_q) {
       f32x16 o = zero16();
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        o = mma32(*reinterpret_cast<const bf16x8*>(dSs + n * C::PKT + 16 * kc + 8 * hf), ktf[kc], o);
-      const size_t row0 = ((size_t)b * N + row_t[0]) * H_q + g * G;
+      for (int kc = 0; kc < 8; ++kc) o = mma32(trfrag(dSt, C::PST, 0, kc, lane), ktf[kc], o);
+      const int id0 = max(tb[kRowId * 32], 0);
 #pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        const int r = c_row(vv, lane);
-        const int tr = row_t[r];
-        const size_t row = tr >= 0 ? ((size_t)b * N + tr) * H_q + g * G + r % G : row0;
-        atomicAdd(dq_acc + row * D + qcol, tr >= 0 ? o[vv] : 0.f);
+      for (int grp = 0; grp < 4; ++grp) {
+        const int4 id4 = *reinterpret_cast<const int4*>(tb + kRowId * 32 + 8 * grp + 4 * hf);
+        const int ids[4] = {id4.x, id4.y, id4.z, id4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int vv = 4 * grp + e;
+          atomicAdd(dq_acc + (size_t)(ids[e] >= 0 ? ids[e] : id0) * D + qcol, ids[e] >= 0 ? o[vv] : 0.f);
+        }
       }
     }
     {
       f32x16 o = zero16();
 #pragma unroll
       for (int kc = 0; kc < KCW; ++kc) {
-        const int k0 = 16 * (kpart * KCW + kc) + 8 * hf;
-        o = mma32(*reinterpret_cast<const bf16x8*>(dZs + n * C::PKT + k0),
-                  *reinterpret_cast<const bf16x8*>(KIt + (32 * itile + n) * C::PKT + k0), o);
+        const int kq = kpart * KCW + kc;
+        o = mma32(trfrag(dZt, C::PST, 0, kq, lane),
+                  *reinterpret_cast<const bf16x8*>(KIt + (32 * itile + n) * C::PKT + 16 * kq + 8 * hf), o);
       }
-      const size_t qrow0 = ((size_t)b * N + qry_t[0]) * H_kv + g;
+      const int qid0 = max(tb[kQryId * 32], 0);
 #pragma unroll
       for (int vv = 0; vv < NVQ; ++vv) {
         const int qr = c_row(vv, lane);
-        const int tq = qr < TQ ? qry_t[qr] : -1;
-        const size_t row = tq >= 0 ? ((size_t)b * N + tq) * H_kv + g : qrow0;
-        atomicAdd(dq_idx + row * DIDX + 32 * itile + n, tq >= 0 ? o[vv] : 0.f);
+        if (qr < TQ) {
+          const int id = tb[kQryId * 32 + qr];
+          atomicAdd(dq_idx + (size_t)(id >= 0 ? id : qid0) * DIDX + 32 * itile + n, id >= 0 ? o[vv] : 0.f);
+        }
       }
     }
-    if (EXTRA && kl != nullptr && threadIdx.x < TQ && qry_t[threadIdx.x] >= 0)
-      atomicAdd(&kl[((size_t)b * N + qry_t[threadIdx.x]) * H_kv + g], qry_kl[threadIdx.x]);
+    if (EXTRA && kl != nullptr && threadIdx.x < TQ && tb[kQryId * 32 + threadIdx.x] >= 0)
+      atomicAdd(&kl[tb[kQryId * 32 + threadIdx.x]], tf[kQryKl * 32 + threadIdx.x]);
     // Step st + 1's tiles: nothing reads Qs / dOs / QIs or the other table set
-    // after the barrier that closed (d), so this can overlap the atomics.
+    // after the barrier above, so this can overlap the atomics.
     store_step(st + 1);
   }
 
   // Flush the block's dK, dV (group g) and dk_idx (shared by the groups)
   // through LDS, so that each atomic instruction covers two 32-float runs of
   // one key row instead of 32 rows.
-  float* scr = reinterpret_cast<float*>(smem + C::OFF_DS) + wave * 32 * 33;
+  float* scr = reinterpret_cast<float*>(smem + C::OFF_QS) + wave * 32 * 33;
   auto flush = [&](const f32x16& acc, float* dst_row0, size_t row_stride) {
     __syncthreads();
 #pragma unroll
