@@ -33,6 +33,8 @@
 //   bwd_finalize_kernel  fp32 accumulators -> bf16 dq, dk, dv.
 #include "msa_internal.h"
 
+#include <type_traits>
+
 namespace msa {
 namespace {
 
@@ -240,23 +242,47 @@ enum : int {
   kNumTabs
 };
 
+// Row-major bf16 tiles in LDS.  Pad<P>: rows of P elements.  Swz128: rows of
+// 128 elements (256 B, no padding) whose 16-byte chunk c of row r is stored at
+// chunk c ^ (4 (r & 3) + ((r >> 2) & 3)); a read of one chunk from each of 16
+// consecutive rows and a transpose read of 4 consecutive rows x 2 chunks then
+// both touch 16 distinct chunks, so neither has an LDS bank conflict.
+template <int P>
+struct Pad {
+  static constexpr int pitch = P;
+  __device__ static int off(int r, int c) { return r * P + c; }
+};
+struct Swz128 {
+  static constexpr int pitch = 128;
+  __device__ static int off(int r, int c) {   // c: a multiple of 4
+    return r * 128 + (((c >> 3) ^ (4 * (r & 3) + ((r >> 2) & 3))) << 3) + (c & 7);
+  }
+};
+template <int W>
+using TileOf = typename std::conditional<W == 128, Swz128, Pad<W + 8>>::type;
+
 template <int D, int DIDX>
 struct BwdCfg {
-  static constexpr int PKT = kBlock + 8;   // K_idx^T rows of 128 keys (+16 B)
-  static constexpr int PQ = D + 8;         // Q / dO rows (+16 B)
-  static constexpr int PQI = DIDX + 8;     // q_idx rows (+16 B)
-  static constexpr int PST = 32 + 4;       // dS^T / dz^T: one row of 32 step rows per key (+8 B)
+  using TQ = TileOf<D>;                    // Q, dO, K, V tiles
+  using TI = Pad<DIDX + 8>;                // q_idx, K_idx tiles
+  using TS = Pad<32 + 4>;                  // dS^T, dz^T: one row of 32 step rows per key
+  static constexpr int PQ = TQ::pitch;
+  static constexpr int PQI = TI::pitch;
+  static constexpr int PST = TS::pitch;
   static constexpr size_t OFF_QS = 0;                                    // Q        [32][PQ]
   static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;        // dO       [32][PQ]
   static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;       // q_idx    [32][PQI]
   static constexpr size_t OFF_DST = OFF_QIS + (size_t)32 * PQI * 2;      // dS^T     [128][PST]
-  static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     [128][PST]
-  static constexpr size_t OFF_TAB = OFF_DZT + (size_t)kBlock * PST * 2;  // 2 x kNumTabs x [32]
-  static constexpr size_t OFF_KIT = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K_idx^T [DIDX][PKT]
-  static constexpr size_t OFF_QL = OFF_KIT + (size_t)DIDX * PKT * 2;     // item queries: (t << 6) | slot
+  static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     2 x [128][PST]
+  static constexpr size_t OFF_TAB = OFF_DZT + (size_t)2 * kBlock * PST * 2;   // 2 x kNumTabs x [32]
+  static constexpr size_t OFF_KS = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K of the block  [128][PQ]
+  static constexpr size_t OFF_VS = OFF_KS + (size_t)kBlock * PQ * 2;     // V of the block     [128][PQ]
+  static constexpr size_t OFF_KIS = OFF_VS + (size_t)kBlock * PQ * 2;    // K_idx of the block [128][PQI]
+  static constexpr size_t OFF_QL = OFF_KIS + (size_t)kBlock * PQI * 2;   // item queries: (t << 6) | slot
   static constexpr size_t LDS = OFF_QL + (size_t)(kBlock + kBigItem) * 4;
   // The flush at the end of an item reuses [OFF_QS, OFF_TAB) as 4 x [32][33] fp32.
   static_assert(OFF_TAB - OFF_QS >= 4 * 32 * 33 * 4, "flush scratch");
+  static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
 
 // A work item of the main kernel and the queries it covers: item-local query
@@ -316,33 +342,25 @@ __device__ inline int big_query(const BigItem& it, int qi, const int32_t* __rest
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // A operand X^T of a 32x32x16 MFMA read straight from a row-major [rows][cols]
-// bf16 LDS tile with the gfx950 transpose read (within each group of 16
+// bf16 LDS tile of layout L with the gfx950 transpose read (within each group of 16
 // lanes, lane i receives element i % 4 of the vectors addressed by lanes
 // 4k + i / 4, k = 0..3; checked on hardware): lane l gets column m0 + l % 32
 // and the K values of rows r0 .. r0+3 (slots 0..3) and r0+8 .. r0+11
 // (slots 4..7), with r0 = 16 kc + 4 (l / 32) - the row order of a C-layout
 // tile's slots 8 kc .. 8 kc + 7.
-__device__ inline bf16x8 trfrag(const bf16* base, int pitch, int m0, int kc, int lane) {
+template <class L>
+__device__ inline bf16x8 trfrag(const bf16* base, int m0, int kc, int lane) {
   const int jj = lane & 15;
   const int r0 = 16 * kc + 4 * (lane >> 5) + (jj >> 2);
   const int col = m0 + 16 * ((lane >> 4) & 1) + 4 * (jj & 3);
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + r0 * pitch + col));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + (r0 + 8) * pitch + col));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + L::off(r0, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + L::off(r0 + 8, col)));
   const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
   bf16x8 r;
   r[0] = l4[0]; r[1] = l4[1]; r[2] = l4[2]; r[3] = l4[3];
   r[4] = h4[0]; r[5] = h4[1]; r[6] = h4[2]; r[7] = h4[3];
   return r;
-}
-// Key of K slot i of half-wave hf in 16-key chunk kc, in the order trfrag
-// delivers it (see above).
-__device__ inline int tr_key(int kc, int hf, int i) { return 16 * kc + 4 * hf + (i & 3) + 8 * (i >> 2); }
-// Position that key kk takes in a row stored so that a plain 16-byte read at
-// 16 kc + 8 hf yields the keys tr_key(kc, hf, 0..7).
-__device__ inline int tr_pos(int kk) {
-  const int r = kk & 15;
-  return (kk & ~15) + 8 * ((r >> 2) & 1) + (r & 3) + 4 * (r >> 3);
 }
 // Matching B operand: slots 8kc .. 8kc+7 of a C-layout tile.
 __device__ inline bf16x8 cfrag(const f32x16& x, int kc) {
@@ -423,12 +441,15 @@ __device__ inline f32x16 head_mean(const f32x16& p, int hf) {
 // 32x32x16 MFMA tiles (C-layout: lane l holds column l % 32, rows
 // 8*(v/4) + 4*(l/32) + v%4 in slot v; A/B operands: lane l holds row/column
 // l % 32 and k = 8*(l/32) + i).  Per step of 32 (query, head) rows:
-//   S = Q K_w^T, dP = dO V_w^T, r = q_idx K_idx,w^T  (A from LDS, B in registers)
+//   S = Q K_w^T, dP = dO V_w^T, r = q_idx K_idx,w^T  (A and B from LDS tiles)
 //   P, dS; the head-mean teacher pbar, p_px and dz    (lane = key, all in registers)
 //   dV_w^T += dO^T P, dK_w^T += Q^T dS, dk_idx_w^T += q_idx^T dz
 //   dS^T, dz^T -> LDS; barrier
-//   dQ[:, 32w..32w+31] = dS K and dq_idx = dz K_idx  (A by transpose reads of dS^T /
-//                                        dz^T, B = K^T / K_idx^T in the matching key order)
+//   dQ[:, 32w..32w+31] = dS K and dq_idx = dz K_idx  (A and B by transpose reads of
+//                                        dS^T / dz^T and of the K / K_idx tiles)
+// The block's K, V and K_idx stay in LDS for the whole item and every MFMA
+// operand is read from LDS, which leaves the registers to the accumulators
+// and to operands fetched ahead of their MFMAs.
 // ---------------------------------------------------------------------------
 template <int D, int DIDX, int G, bool EXTRA>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
@@ -460,9 +481,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   bf16* dOs = reinterpret_cast<bf16*>(smem + C::OFF_DOS);
   bf16* QIs = reinterpret_cast<bf16*>(smem + C::OFF_QIS);
   bf16* dSt = reinterpret_cast<bf16*>(smem + C::OFF_DST);
-  bf16* dZt = reinterpret_cast<bf16*>(smem + C::OFF_DZT);
+  bf16* dZt2 = reinterpret_cast<bf16*>(smem + C::OFF_DZT);   // dz^T of steps of either parity
   int* tabs = reinterpret_cast<int*>(smem + C::OFF_TAB);
-  bf16* KIt = reinterpret_cast<bf16*>(smem + C::OFF_KIT);
+  bf16* Ks = reinterpret_cast<bf16*>(smem + C::OFF_KS);
+  bf16* Vs = reinterpret_cast<bf16*>(smem + C::OFF_VS);
+  bf16* KIs = reinterpret_cast<bf16*>(smem + C::OFF_KIS);
   int* qlist = reinterpret_cast<int*>(smem + C::OFF_QL);   // (t << 6) | slot, or -1
 
   BigItem it;
@@ -473,7 +496,6 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   const int b = it.b, g = it.g, j = it.j;
   const int key = 32 * wave + n;                      // this lane's key inside the block
   const int u = j * kBlock + key;
-  const size_t kv_row = ((size_t)b * N + u) * H_kv + g;
   const size_t blk_row0 = ((size_t)b * N + (size_t)j * kBlock) * H_kv + g;   // key 0 of the block
   const int nq = it.n_own + it.ne;
   const bool want_slot = EXTRA && dscore != nullptr;
@@ -486,39 +508,25 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     const int t = big_query(it, qi, block_idx, N, H_kv, topk, want_slot, &slot);
     qlist[qi] = t < 0 ? -1 : ((t << 6) | slot);
   }
-  // K_idx^T of the block in LDS (B operand of dq_idx), keys in the order of
-  // the transpose-read A operand.
-  for (int c = threadIdx.x; c < kBlock * (DIDX / 8); c += kMainThreads) {
-    const int kk = c / (DIDX / 8), col = (c % (DIDX / 8)) * 8;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
-    const int pk = tr_pos(kk);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) KIt[(col + i) * C::PKT + pk] = x[i];
+  // K, V and K_idx of the block in LDS, row-major (one row per key).
+  for (int c = threadIdx.x; c < kBlock * CPR; c += kMainThreads) {
+    const int kk = c / CPR, col = (c % CPR) * 8;
+    const size_t row = blk_row0 + (size_t)kk * H_kv;
+    *reinterpret_cast<bf16x8*>(Ks + C::TQ::off(kk, col)) = *reinterpret_cast<const bf16x8*>(k + row * D + col);
+    *reinterpret_cast<bf16x8*>(Vs + C::TQ::off(kk, col)) = *reinterpret_cast<const bf16x8*>(v + row * D + col);
   }
-  // Register operands for the whole item: this wave's 32 keys of K, V, K_idx
-  // (B of S, dP, r: lane = key, K = d), and K^T of the wave's 32 dQ columns
-  // (B of dQ: lane = column, K = keys in transpose-read order).
-  bf16x8 kf[KS], vf[KS], kif[KSI], ktf[8];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = *reinterpret_cast<const bf16x8*>(k + kv_row * D + 16 * ks + 8 * hf);
-    vf[ks] = *reinterpret_cast<const bf16x8*>(v + kv_row * D + 16 * ks + 8 * hf);
+  for (int c = threadIdx.x; c < kBlock * CPRI; c += kMainThreads) {
+    const int kk = c / CPRI, col = (c % CPRI) * 8;
+    *reinterpret_cast<bf16x8*>(KIs + C::TI::off(kk, col)) =
+        *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
   }
-#pragma unroll
-  for (int ks = 0; ks < KSI; ++ks)
-    kif[ks] = *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + u) * DIDX + 16 * ks + 8 * hf);
-  const int qcol = 32 * wave + n;                     // dQ column (wave < DT)
-  const bool has_q = DT == kBwdWaves || wave < DT;
+  const bool has_q = DT == kBwdWaves || wave < DT;   // the wave owns dQ columns 32w..32w+31
   // dq_idx: output tile wave % DTI, over the 16-key chunks
   // [kpart * KCW, (kpart + 1) * KCW), so every wave issues the same atomics.
   constexpr int KPARTS = kBwdWaves / DTI;
   constexpr int KCW = 8 / KPARTS;
   const int itile = wave % DTI, kpart = wave / DTI;
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc)
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      ktf[kc][i] = has_q ? k[(blk_row0 + (size_t)tr_key(kc, hf, i) * H_kv) * D + qcol] : (bf16)0.f;
+  const int qcol = 32 * wave + n;                     // dQ column (wave < DT)
 
   f32x16 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
 #pragma unroll
@@ -528,17 +536,23 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   }
 #pragma unroll
   for (int i = 0; i < DTI; ++i) acc_dki[i] = zero16();
-  __syncthreads();   // item query list and K_idx^T ready
+  __syncthreads();   // item query list and the K, V, K_idx tiles ready
 
-  // Per-thread share of a step, loaded one step ahead into registers: LDM
+  // Per-thread share of a step, loaded into registers one step ahead: LDM
   // 16-byte chunks of Q and dO (with LSE, D, cut-off and id of the rows whose
   // first chunk it holds), one chunk of q_idx, and - for threads < TQ - the
-  // step's query table entry.  The query-list entries these loads need are
-  // read from LDS one step earlier still (pk_*), so issuing the loads waits
-  // for nothing.
-  bf16x8 pre_q[LDM], pre_d[LDM], pre_qi = bf16x8{};
-  float pre_lse[LDM], pre_D[LDM], pre_qlse = 0.f;
-  int pre_t[LDM], pre_cut[LDM], pre_id[LDM], pre_qt = -1, pre_qslot = 0, pre_qcut = -1, pre_qid = -1;
+  // step's query table entry.  The loads of step st + 1 are issued at the top
+  // of step st, before its atomics; the vector-memory counter completes in
+  // order, so the wait for them at the end of the step covers nothing issued
+  // later, as long as every memory operation in between is unconditional and
+  // can be counted.  The query-list entries the loads need are read from LDS
+  // one step before they are issued (pk_*).
+  struct Pre {
+    bf16x8 q[LDM], d[LDM], qi;
+    float lse[LDM], rd[LDM], qlse;
+    int t[LDM], cut[LDM], id[LDM], qt, qslot, qcut, qid;
+  };
+  Pre pre;
   int pk_e[LDM], pk_qi = -1, pk_qt = -1;
   const int ld_col = (threadIdx.x % CPR) * 8;
   const int ld_qr = threadIdx.x / CPRI, ld_qcol = (threadIdx.x % CPRI) * 8;
@@ -552,93 +566,123 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     pk_qi = ld_qr < TQ ? entry(st * TQ + ld_qr) : -1;
     pk_qt = tx < TQ ? entry(st * TQ + tx) : -1;
   };
-  // Every load below is unconditional (clamped to a valid row) so that the
-  // compiler can count them exactly and later wait for them without also
-  // waiting for the atomics issued after them.
-  auto load_step = [&](int st) {
+  // Every load below is unconditional (clamped to a valid row; past the end
+  // of the item it re-reads valid rows, unused) so that the compiler can count
+  // the memory operations exactly.
+  auto load_step = [&](int st, Pre& x) {
 #pragma unroll
     for (int c = 0; c < LDM; ++c) {
       const int r = (threadIdx.x + c * kMainThreads) / CPR;
       const int t = pk_e[c] < 0 ? -1 : (pk_e[c] >> 6);
-      pre_t[c] = t;
-      pre_cut[c] = cutoff((32 * st + r) / G, t);
+      x.t[c] = t;
+      x.cut[c] = cutoff((32 * st + r) / G, t);
       const size_t qrow = ((size_t)b * N + (t < 0 ? 0 : t)) * H_q + g * G + r % G;
-      pre_id[c] = t < 0 ? -1 : (int)qrow;
-      pre_q[c] = *reinterpret_cast<const bf16x8*>(q + qrow * D + ld_col);
-      pre_d[c] = *reinterpret_cast<const bf16x8*>(dO + qrow * D + ld_col);
-      pre_lse[c] = lse[qrow];
-      pre_D[c] = Dv[qrow];
+      x.id[c] = t < 0 ? -1 : (int)qrow;
+      x.q[c] = *reinterpret_cast<const bf16x8*>(q + qrow * D + ld_col);
+      x.d[c] = *reinterpret_cast<const bf16x8*>(dO + qrow * D + ld_col);
+      x.lse[c] = lse[qrow];
+      x.rd[c] = Dv[qrow];
     }
     {
       const int tq = pk_qi < 0 ? -1 : (pk_qi >> 6);
-      pre_qi = *reinterpret_cast<const bf16x8*>(q_idx + (((size_t)b * N + (tq < 0 ? 0 : tq)) * H_kv + g) * DIDX +
-                                                ld_qcol);
-      if (tq < 0) pre_qi = bf16x8{};
+      x.qi = *reinterpret_cast<const bf16x8*>(q_idx + (((size_t)b * N + (tq < 0 ? 0 : tq)) * H_kv + g) * DIDX +
+                                              ld_qcol);
+      if (tq < 0) x.qi = bf16x8{};
     }
     {
-      pre_qt = pk_qt < 0 ? -1 : (pk_qt >> 6);
-      pre_qslot = pk_qt < 0 ? 0 : (pk_qt & 63);
-      pre_qcut = cutoff(st * TQ + tx, pre_qt);
-      const size_t qrow = ((size_t)b * N + (pre_qt < 0 ? 0 : pre_qt)) * H_kv + g;
-      pre_qid = pre_qt < 0 ? -1 : (int)qrow;
-      pre_qlse = lse_idx[qrow];
+      x.qt = pk_qt < 0 ? -1 : (pk_qt >> 6);
+      x.qslot = pk_qt < 0 ? 0 : (pk_qt & 63);
+      x.qcut = cutoff(st * TQ + tx, x.qt);
+      const size_t qrow = ((size_t)b * N + (x.qt < 0 ? 0 : x.qt)) * H_kv + g;
+      x.qid = x.qt < 0 ? -1 : (int)qrow;
+      x.qlse = lse_idx[qrow];
     }
   };
   // Store a step's prefetched registers into its LDS tiles and tables.
-  auto store_step = [&](int st) {
+  auto store_step = [&](int st, const Pre& x) {
     int* tb = tabs + (st & 1) * NT;
     float* tf = reinterpret_cast<float*>(tb);
 #pragma unroll
     for (int c = 0; c < LDM; ++c) {
       const int r = (threadIdx.x + c * kMainThreads) / CPR;
-      *reinterpret_cast<bf16x8*>(Qs + r * C::PQ + ld_col) = pre_q[c];
-      *reinterpret_cast<bf16x8*>(dOs + r * C::PQ + ld_col) = pre_d[c];
+      *reinterpret_cast<bf16x8*>(Qs + C::TQ::off(r, ld_col)) = x.q[c];
+      *reinterpret_cast<bf16x8*>(dOs + C::TQ::off(r, ld_col)) = x.d[c];
       if (ld_col == 0) {
-        tb[kRowT * 32 + r] = pre_t[c];
-        tb[kRowCut * 32 + r] = pre_cut[c];
-        tf[kRowLse * 32 + r] = pre_lse[c] * kLog2e;
-        tf[kRowD * 32 + r] = pre_D[c];
-        tb[kRowId * 32 + r] = pre_id[c];
+        tb[kRowT * 32 + r] = x.t[c];
+        tb[kRowCut * 32 + r] = x.cut[c];
+        tf[kRowLse * 32 + r] = x.lse[c] * kLog2e;
+        tf[kRowD * 32 + r] = x.rd[c];
+        tb[kRowId * 32 + r] = x.id[c];
       }
     }
-    if (ld_idx) *reinterpret_cast<bf16x8*>(QIs + ld_qr * C::PQI + ld_qcol) = pre_qi;
+    if (ld_idx) *reinterpret_cast<bf16x8*>(QIs + C::TI::off(ld_qr, ld_qcol)) = x.qi;
     if (threadIdx.x < 32) {
-      tb[kQryT * 32 + tx] = pre_qt;
-      tb[kQrySlot * 32 + tx] = pre_qslot;
-      tb[kQryCut * 32 + tx] = pre_qcut;
-      tf[kQryLse * 32 + tx] = pre_qlse * kLog2e;
+      tb[kQryT * 32 + tx] = x.qt;
+      tb[kQrySlot * 32 + tx] = x.qslot;
+      tb[kQryCut * 32 + tx] = x.qcut;
+      tf[kQryLse * 32 + tx] = x.qlse * kLog2e;
       tf[kQryKl * 32 + tx] = 0.f;
-      tb[kQryId * 32 + tx] = pre_qid;
+      tb[kQryId * 32 + tx] = x.qid;
     }
   };
 
   const float c_s = scale * kLog2e;
   const float c_i = scale_idx * kLog2e;
   const int n_steps = (nq * G + 31) / 32;
+
+  // dq_idx[queries, tile] = dz K_idx over this wave's share of the keys
+  // (lane = d_idx column, slots = queries), for step st.  It runs at the top
+  // of step st + 1, before that step's loads are issued: its atomics are
+  // conditional, so the compiler cannot count them, and there they sit
+  // behind no load that has to be waited for.  dz^T is double buffered for it.
+  auto dq_idx_step = [&](int st) {
+    const int* tb = tabs + (st & 1) * NT;
+    const bf16* dZt = dZt2 + (st & 1) * kBlock * C::PST;
+    f32x16 o = zero16();
+#pragma unroll
+    for (int kc = 0; kc < KCW; ++kc) {
+      const int kq = kpart * KCW + kc;
+      o = mma32(trfrag<typename C::TS>(dZt, 0, kq, lane), trfrag<typename C::TI>(KIs, 32 * itile, kq, lane), o);
+    }
+    const int qid0 = max(tb[kQryId * 32], 0);
+#pragma unroll
+    for (int vv = 0; vv < NVQ; ++vv) {
+      const int qr = c_row(vv, lane);
+      if (qr < TQ) {
+        const int id = tb[kQryId * 32 + qr];
+        atomicAdd(dq_idx + (size_t)(id >= 0 ? id : qid0) * DIDX + 32 * itile + n, id >= 0 ? o[vv] : 0.f);
+      }
+    }
+  };
+
   peek(0);
-  load_step(0);
-  store_step(0);
+  load_step(0, pre);
+  store_step(0, pre);
   peek(1);
 #pragma unroll 1
   for (int st = 0; st < n_steps; ++st) {
     asm volatile("" ::: "memory");
     const int* tb = tabs + (st & 1) * NT;
     const float* tf = reinterpret_cast<const float*>(tb);
-    __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T / dz^T consumed
-    // Prefetch step st + 1 (past the end it re-reads valid rows, unused).
-    load_step(st + 1);
+    __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T consumed
+    if (st > 0) dq_idx_step(st - 1);
+    load_step(st + 1, pre);
     peek(st + 2);
 
     // S, dP, index logits (lane = key, slots = rows / queries).
     f32x16 s = zero16(), dp = zero16(), ri = zero16();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = mma32(*reinterpret_cast<const bf16x8*>(Qs + n * C::PQ + 16 * ks + 8 * hf), kf[ks], s);
-      dp = mma32(*reinterpret_cast<const bf16x8*>(dOs + n * C::PQ + 16 * ks + 8 * hf), vf[ks], dp);
+      // S: A = Q rows (lane = row n), B = K rows (lane = key); dP likewise.
+      s = mma32(*reinterpret_cast<const bf16x8*>(Qs + C::TQ::off(n, 16 * ks + 8 * hf)),
+                *reinterpret_cast<const bf16x8*>(Ks + C::TQ::off(key, 16 * ks + 8 * hf)), s);
+      dp = mma32(*reinterpret_cast<const bf16x8*>(dOs + C::TQ::off(n, 16 * ks + 8 * hf)),
+                 *reinterpret_cast<const bf16x8*>(Vs + C::TQ::off(key, 16 * ks + 8 * hf)), dp);
     }
 #pragma unroll
     for (int ks = 0; ks < KSI; ++ks)
-      ri = mma32(*reinterpret_cast<const bf16x8*>(QIs + n * C::PQI + 16 * ks + 8 * hf), kif[ks], ri);
+      ri = mma32(*reinterpret_cast<const bf16x8*>(QIs + C::TI::off(n, 16 * ks + 8 * hf)),
+                 *reinterpret_cast<const bf16x8*>(KIs + C::TI::off(key, 16 * ks + 8 * hf)), ri);
     // P, dS; dS^T to LDS.
     f32x16 p, ds;
 #pragma unroll
@@ -690,7 +734,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
         }
       }
       if (r4 < TQ)
-        *reinterpret_cast<bf16x4*>(dZt + key * C::PST + r4) =
+        *reinterpret_cast<bf16x4*>(dZt2 + (st & 1) * kBlock * C::PST + key * C::PST + r4) =
             pack4(dz[4 * gq] * scale_idx, dz[4 * gq + 1] * scale_idx, dz[4 * gq + 2] * scale_idx,
                   dz[4 * gq + 3] * scale_idx);
     }
@@ -700,8 +744,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
       const bf16x8 pbf = cfrag(p, kc), sbf = cfrag(ds, kc);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        acc_dv[dt] = mma32(trfrag(dOs, C::PQ, 32 * dt, kc, lane), pbf, acc_dv[dt]);
-        acc_dk[dt] = mma32(trfrag(Qs, C::PQ, 32 * dt, kc, lane), sbf, acc_dk[dt]);
+        acc_dv[dt] = mma32(trfrag<typename C::TQ>(dOs, 32 * dt, kc, lane), pbf, acc_dv[dt]);
+        acc_dk[dt] = mma32(trfrag<typename C::TQ>(Qs, 32 * dt, kc, lane), sbf, acc_dk[dt]);
       }
     }
     {
@@ -712,21 +756,23 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
       for (int kc = 0; kc < KCQ; ++kc) {
         const bf16x8 zb = cfrag(zs, kc);
 #pragma unroll
-        for (int dt = 0; dt < DTI; ++dt) acc_dki[dt] = mma32(trfrag(QIs, C::PQI, 32 * dt, kc, lane), zb, acc_dki[dt]);
+        for (int dt = 0; dt < DTI; ++dt)
+          acc_dki[dt] = mma32(trfrag<typename C::TI>(QIs, 32 * dt, kc, lane), zb, acc_dki[dt]);
       }
     }
     __syncthreads();   // dS^T, dz^T and the KL partials complete
 
-    // dQ[rows, wave's 32 columns] = dS K and dq_idx[queries, tile] = dz K_idx
-    // (this wave's share of the keys): lane = output column, slots = rows, so
-    // each atomic instruction covers 32 consecutive floats of one row per
-    // half-wave.  A row without a query adds 0 at the step's first row (always
-    // a real one) instead of branching: the number of atomics per step stays
-    // fixed and the loads of the next step can be waited for alone.
+    // dQ[rows, wave's 32 columns] = dS K (this wave's share of the keys): lane
+    // = output column, slots = rows, so each atomic instruction covers 32
+    // consecutive floats of one row per half-wave.  A row without a query adds
+    // 0 at the step's first row (always a real one) instead of branching, so
+    // the number of memory operations after the loads is fixed and the wait
+    // for them at the end of the step covers none of these atomics.
     if (has_q) {
       f32x16 o = zero16();
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) o = mma32(trfrag(dSt, C::PST, 0, kc, lane), ktf[kc], o);
+      for (int kc = 0; kc < 8; ++kc)
+        o = mma32(trfrag<typename C::TS>(dSt, 0, kc, lane), trfrag<typename C::TQ>(Ks, 32 * wave, kc, lane), o);
       const int id0 = max(tb[kRowId * 32], 0);
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
@@ -739,30 +785,13 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
         }
       }
     }
-    {
-      f32x16 o = zero16();
-#pragma unroll
-      for (int kc = 0; kc < KCW; ++kc) {
-        const int kq = kpart * KCW + kc;
-        o = mma32(trfrag(dZt, C::PST, 0, kq, lane),
-                  *reinterpret_cast<const bf16x8*>(KIt + (32 * itile + n) * C::PKT + 16 * kq + 8 * hf), o);
-      }
-      const int qid0 = max(tb[kQryId * 32], 0);
-#pragma unroll
-      for (int vv = 0; vv < NVQ; ++vv) {
-        const int qr = c_row(vv, lane);
-        if (qr < TQ) {
-          const int id = tb[kQryId * 32 + qr];
-          atomicAdd(dq_idx + (size_t)(id >= 0 ? id : qid0) * DIDX + 32 * itile + n, id >= 0 ? o[vv] : 0.f);
-        }
-      }
-    }
     if (EXTRA && kl != nullptr && threadIdx.x < TQ && tb[kQryId * 32 + threadIdx.x] >= 0)
       atomicAdd(&kl[tb[kQryId * 32 + threadIdx.x]], tf[kQryKl * 32 + threadIdx.x]);
     // Step st + 1's tiles: nothing reads Qs / dOs / QIs or the other table set
     // after the barrier above, so this can overlap the atomics.
-    store_step(st + 1);
+    store_step(st + 1, pre);
   }
+  dq_idx_step(n_steps - 1);   // dz^T of the last step is complete (barrier before its dQ)
 
   // Flush the block's dK, dV (group g) and dk_idx (shared by the groups)
   // through LDS, so that each atomic instruction covers two 32-float runs of
