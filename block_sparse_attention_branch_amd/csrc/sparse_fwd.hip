@@ -151,8 +151,20 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_rows = nq * G;
   const float c_exp = scale * kLog2e;
+  // The list entries of this lane's row in each of the wave's row tiles (at
+  // most kItemQueries * G / 128 of them), read up front so that no row tile
+  // waits for an entry before it can load its queries.
+  constexpr int kTiles = kItemQueries * G / 128;
+  int ents[kTiles];
+  if (!diag) {
+#pragma unroll
+    for (int i = 0; i < kTiles; ++i) {
+      const int r = wave * 32 + i * 128 + (lane & 31);
+      ents[i] = r < n_rows ? ent[r / G] : 0;
+    }
+  }
 #pragma unroll 1
-  for (int r0 = wave * 32; r0 < n_rows; r0 += 128) {
+  for (int r0 = wave * 32, tile = 0; r0 < n_rows; r0 += 128, ++tile) {
     // Keep the K/V fragment reads inside the loop (re-read from LDS per row
     // tile) instead of letting them be hoisted into ~256 live registers.
     asm volatile("" ::: "memory");
@@ -166,7 +178,10 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
       for (int e = 0; e < topk; ++e)
         if (brow[e] == j) slot = e;
     } else {
-      const int e = ent[min(qi, nq - 1)];
+      int e = ents[0];
+#pragma unroll
+      for (int i = 1; i < kTiles; ++i)
+        if (tile == i) e = ents[i];
       t = e >> 6;
       slot = e & 63;
       // A well-formed map only yields queries of this chunk; anything else is
@@ -252,7 +267,13 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
   }
 }
 
-// Merge the per-block partials of every (query, head) of the chunk.
+// Merge the per-block partials of every (query, head) of the chunk: LPR lanes
+// per (query, head) row, 16 bytes of o each.  The slot weights come first
+// (LSE over the valid slots); then the partials are read 8 slots at a time
+// with all 8 loads in flight, so the kernel streams at memory speed instead
+// of waiting on one load per slot.  Padded slots (block index -1) hold
+// unwritten memory: they are excluded by selection, never by multiplying
+// with a zero weight.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po, const float* __restrict__ plse,
                                                         const int32_t* __restrict__ block_idx, T* __restrict__ o,
@@ -260,6 +281,8 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po
                                                         int topk, int c0, int CQ) {
   constexpr int EPL = 16 / (int)sizeof(T);   // elements per lane
   constexpr int LPR = D / EPL;               // lanes per row
+  constexpr int MAXK = 32;                   // largest supported topk
+  constexpr int CH = 8;                      // slots per batch of loads
   const int H_q = H_kv * G;
   const size_t row = (size_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   if (row >= (size_t)B * CQ * H_q) return;
@@ -270,24 +293,56 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po
   const int t = c0 + tl, g = h / G;
   const int32_t* brow = block_idx + (((size_t)b * N + t) * H_kv + g) * topk;
   const float* lrow = plse + row * topk;
+  // Slot log-sum-exps in log2 units, -inf for padded slots.
+  float lv[MAXK];
+#pragma unroll
+  for (int e = 0; e < MAXK; ++e) lv[e] = -INFINITY;
+  if ((topk & 3) == 0) {   // rows of 16-byte multiples: vector reads
+#pragma unroll
+    for (int e = 0; e < MAXK; e += 4)
+      if (e < topk) {
+        const int4 bi = *reinterpret_cast<const int4*>(brow + e);
+        const float4 l4 = *reinterpret_cast<const float4*>(lrow + e);
+        lv[e] = bi.x >= 0 ? l4.x * kLog2e : -INFINITY;
+        lv[e + 1] = bi.y >= 0 ? l4.y * kLog2e : -INFINITY;
+        lv[e + 2] = bi.z >= 0 ? l4.z * kLog2e : -INFINITY;
+        lv[e + 3] = bi.w >= 0 ? l4.w * kLog2e : -INFINITY;
+      }
+  } else {
+#pragma unroll
+    for (int e = 0; e < MAXK; ++e)
+      if (e < topk) lv[e] = brow[e] >= 0 ? lrow[e] * kLog2e : -INFINITY;
+  }
   float mx = -INFINITY;
-  for (int e = 0; e < topk; ++e)
-    if (brow[e] >= 0) mx = fmaxf(mx, lrow[e]);
+#pragma unroll
+  for (int e = 0; e < MAXK; ++e) mx = fmaxf(mx, lv[e]);   // finite: the own block is always valid
   float den = 0.f;
-  for (int e = 0; e < topk; ++e)
-    if (brow[e] >= 0) den += expf(lrow[e] - mx);
-  const float L = mx + logf(den);
+#pragma unroll
+  for (int e = 0; e < MAXK; ++e) den += __builtin_amdgcn_exp2f(lv[e] - mx);
+  const float L2 = mx + __builtin_amdgcn_logf(den);   // log2 of the row's total
   float acc[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-  for (int e = 0; e < topk; ++e) {
-    if (brow[e] < 0) continue;
-    const float wgt = expf(lrow[e] - L);
-    const uint4 raw = *reinterpret_cast<const uint4*>(po + (row * topk + e) * D + part * EPL);
-    const T* x = reinterpret_cast<const T*>(&raw);
+  const T* prow = po + row * topk * D + part * EPL;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) acc[i] += wgt * to_f32(x[i]);
+  for (int e0 = 0; e0 < MAXK; e0 += CH) {
+    if (e0 >= topk) break;
+    uint4 raw[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (e0 + i < topk) raw[i] = *reinterpret_cast<const uint4*>(prow + (size_t)(e0 + i) * D);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int e = e0 + i;
+      if (e < topk && lv[e] != -INFINITY) {
+        const float wgt = __builtin_amdgcn_exp2f(lv[e] - L2);
+        const T* x = reinterpret_cast<const T*>(&raw[i]);
+#pragma unroll
+        for (int c = 0; c < EPL; ++c) acc[c] = fmaf(wgt, to_f32(x[c]), acc[c]);
+      }
+    }
   }
+  const float L = L2 * kLn2;
   uint4 outv;
   T* ov = reinterpret_cast<T*>(&outv);
 #pragma unroll
