@@ -44,7 +44,11 @@ struct FwdCfg {
   static constexpr int PV = kBlock + 8 / (int)sizeof(T); // V^T row pitch (elements), 8 B pad
   static constexpr size_t K_BYTES = (size_t)kBlock * PK * sizeof(T);
   static constexpr size_t V_BYTES = (size_t)D * PV * sizeof(T);
-  static constexpr size_t LDS = K_BYTES + V_BYTES;
+  // Per-wave staging of one 32-column slice of the partial output (32 rows),
+  // so that the partials leave in 16-byte pieces, 64 bytes per row per slice.
+  static constexpr int PO = 32 + 16 / (int)sizeof(T);                  // row pitch (elements)
+  static constexpr size_t O_BYTES = (size_t)(kFwdThreads / 64) * 32 * PO * sizeof(T);
+  static constexpr size_t LDS = K_BYTES + V_BYTES + O_BYTES;
   static constexpr int DT = D / 32;
   static constexpr int CPR = D * (int)sizeof(T) / 16;    // 16-byte chunks per key row
   static constexpr int EPC = 16 / (int)sizeof(T);        // elements per chunk
@@ -252,17 +256,35 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
         }
     }
 
-    if (valid) {
-      const float inv = 1.f / lsum;
-      const size_t prow = (((size_t)b * CQ + (t - c0)) * H_q + h) * topk + slot;
-      T* dst = po + prow * D + 4 * (lane >> 5);
+    // Partial o of the row (normalised) and its LSE.  Each 32-column slice
+    // goes through the wave's LDS staging tile: lane (row, half) writes its
+    // 4 x 4 values, then lane l stores 16 bytes of row l / RPL (+ 32 / SPL..)
+    // so that each store instruction writes whole 64-byte row segments.
+    const float inv = 1.f / lsum;
+    const int prow = valid ? (((b * CQ + (t - c0)) * H_q + h) * topk + slot) : -1;
+    if (valid && lane < 32) plse[prow] = m * scale + logf(lsum);
+    {
+      constexpr int EPC = C::EPC;                 // elements per 16-byte piece
+      constexpr int PPR = 32 / EPC;               // pieces per 32-column row slice
+      constexpr int RPI = 64 / PPR;               // rows per store instruction
+      T* ost = reinterpret_cast<T*>(smem + C::K_BYTES + C::V_BYTES) + wave * 32 * C::PO;
+      const int rl = lane & 31;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+      for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4)
-          Store4<T>::st(dst + dt * 32 + 8 * v4, o[dt][4 * v4] * inv, o[dt][4 * v4 + 1] * inv,
+          Store4<T>::st(ost + rl * C::PO + 8 * v4 + 4 * (lane >> 5), o[dt][4 * v4] * inv, o[dt][4 * v4 + 1] * inv,
                         o[dt][4 * v4 + 2] * inv, o[dt][4 * v4 + 3] * inv);
-      if (lane < 32) plse[prow] = m * scale + logf(lsum);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's slice is in LDS
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int rr = i * RPI + lane / PPR, pc = lane % PPR;
+          const int dst_row = __shfl(prow, rr);
+          const uint4 x = *reinterpret_cast<const uint4*>(ost + rr * C::PO + pc * EPC);
+          if (dst_row >= 0) *reinterpret_cast<uint4*>(po + (size_t)dst_row * D + dt * 32 + pc * EPC) = x;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slice read before it is overwritten
+      }
     }
   }
 }
