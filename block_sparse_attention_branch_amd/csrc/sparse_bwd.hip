@@ -205,21 +205,8 @@ __global__ __launch_bounds__(256) void idx_lse_merge_kernel(const float2* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Main fused backward.  4 waves; wave w owns keys 32w..32w+31 of the block.
-// 32x32x16 MFMA tiles (C-layout: lane l holds column l % 32, rows
-// 8*(v/4) + 4*(l/32) + v%4 in slot v; A/B operands: lane l holds row/column
-// l % 32 and k = 8*(l/32) + i).  Per step of 32 (query, head) rows:
-//   S = Q K_w^T, dP = dO V_w^T          (A from LDS tiles, B in registers)
-//   P, dS                               (lane = key, slots = rows)
-//   dV_w^T += dO^T P, dK_w^T += Q^T dS  (A from transposed LDS tiles, B = the
-//                                        P / dS registers as they are)
-//   index logits, p_px, teacher, dz, dk_idx_w^T += q_idx^T dz
-//   dQ[:, 32w..32w+31] = dS K, dq_idx = dz K_idx  (K^T / K_idx^T operands of
-//                                        the wave's output columns in registers)
+// Main fused backward: work items, step tables and LDS tile layouts.
 // ---------------------------------------------------------------------------
-constexpr int kBwdWaves = 4;
-constexpr int kMainThreads = kBwdWaves * kWave;
-
 // Work items of the main kernel: the queries of KV block j (its own 128, with
 // the causal mask) together with the first kBigItem entries of its inverted
 // list, or a later run of kBigItem list entries.  Long items keep the
@@ -242,48 +229,25 @@ enum : int {
   kNumTabs
 };
 
-// Row-major bf16 tiles in LDS.  Pad<P>: rows of P elements.  Swz128: rows of
-// 128 elements (256 B, no padding) whose 16-byte chunk c of row r is stored at
-// chunk c ^ (4 (r & 3) + ((r >> 2) & 3)); a read of one chunk from each of 16
-// consecutive rows and a transpose read of 4 consecutive rows x 2 chunks then
-// both touch 16 distinct chunks, so neither has an LDS bank conflict.
+// Row-major bf16 tiles in LDS.  Pad<P>: rows of P elements.
 template <int P>
 struct Pad {
   static constexpr int pitch = P;
   __device__ static int off(int r, int c) { return r * P + c; }
 };
-struct Swz128 {
+// Swz128b: rows of 128 elements (256 B, no padding) whose 16-byte chunk c of
+// row r is stored at chunk c ^ (2 (r & 7) + ((r >> 3) & 1)).  For the 16x16x32
+// operands: a read of one chunk from 16 consecutive rows and a
+// transpose read (32 lanes: 8 consecutive rows x 2 chunks) both hit distinct
+// chunks.
+struct Swz128b {
   static constexpr int pitch = 128;
   __device__ static int off(int r, int c) {   // c: a multiple of 4
-    return r * 128 + (((c >> 3) ^ (4 * (r & 3) + ((r >> 2) & 3))) << 3) + (c & 7);
+    return r * 128 + (((c >> 3) ^ (2 * (r & 7) + ((r >> 3) & 1))) << 3) + (c & 7);
   }
 };
 template <int W>
-using TileOf = typename std::conditional<W == 128, Swz128, Pad<W + 8>>::type;
-
-template <int D, int DIDX>
-struct BwdCfg {
-  using TQ = TileOf<D>;                    // Q, dO, K, V tiles
-  using TI = Pad<DIDX + 8>;                // q_idx, K_idx tiles
-  using TS = Pad<32 + 4>;                  // dS^T, dz^T: one row of 32 step rows per key
-  static constexpr int PQ = TQ::pitch;
-  static constexpr int PQI = TI::pitch;
-  static constexpr int PST = TS::pitch;
-  static constexpr size_t OFF_QS = 0;                                    // Q        [32][PQ]
-  static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;        // dO       [32][PQ]
-  static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;       // q_idx    [32][PQI]
-  static constexpr size_t OFF_DST = OFF_QIS + (size_t)32 * PQI * 2;      // dS^T     [128][PST]
-  static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     2 x [128][PST]
-  static constexpr size_t OFF_TAB = OFF_DZT + (size_t)2 * kBlock * PST * 2;   // 2 x kNumTabs x [32]
-  static constexpr size_t OFF_KS = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K of the block  [128][PQ]
-  static constexpr size_t OFF_VS = OFF_KS + (size_t)kBlock * PQ * 2;     // V of the block     [128][PQ]
-  static constexpr size_t OFF_KIS = OFF_VS + (size_t)kBlock * PQ * 2;    // K_idx of the block [128][PQI]
-  static constexpr size_t OFF_QL = OFF_KIS + (size_t)kBlock * PQI * 2;   // item queries: (t << 6) | slot
-  static constexpr size_t LDS = OFF_QL + (size_t)(kBlock + kBigItem) * 4;
-  // The flush at the end of an item reuses [OFF_QS, OFF_TAB) as 4 x [32][33] fp32.
-  static_assert(OFF_TAB - OFF_QS >= 4 * 32 * 33 * 4, "flush scratch");
-  static_assert(LDS <= 160 * 1024, "LDS of one CU");
-};
+using Tile16Of = typename std::conditional<W == 128, Swz128b, Pad<W + 8>>::type;
 
 // A work item of the main kernel and the queries it covers: item-local query
 // qi < n_own is t = 128 j + qi (diagonal, causal mask); otherwise it is list
@@ -341,118 +305,113 @@ __device__ inline int big_query(const BigItem& it, int qi, const int32_t* __rest
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// A operand X^T of a 32x32x16 MFMA read straight from a row-major [rows][cols]
-// bf16 LDS tile of layout L with the gfx950 transpose read (within each group of 16
-// lanes, lane i receives element i % 4 of the vectors addressed by lanes
-// 4k + i / 4, k = 0..3; checked on hardware): lane l gets column m0 + l % 32
-// and the K values of rows r0 .. r0+3 (slots 0..3) and r0+8 .. r0+11
-// (slots 4..7), with r0 = 16 kc + 4 (l / 32) - the row order of a C-layout
-// tile's slots 8 kc .. 8 kc + 7.
+__device__ inline bf16x4 pack4(float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (bf16)a; r[1] = (bf16)b; r[2] = (bf16)c; r[3] = (bf16)d;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Main fused backward, 16x16x32 formulation.  8 waves; wave w owns keys
+// 16w..16w+15 of the block, which keeps its dK, dV and dk_idx accumulators
+// small enough for two waves per SIMD.  16x16x32 MFMA layouts (lane l,
+// q = l / 16, c = l % 16): A: row c, k = 8q + i; B: column c, k = 8q + i;
+// C: column c, rows 4q + v in slot v.
+// A step covers 32 (query, head) rows in two 16-row tiles.  Row 16 tile + 4q + v
+// of a step holds R = 8q + 4 tile + v, i.e. query R / G and head R % G, so
+// that the lanes of group q hold whole queries (for G <= 8) and the teacher
+// mean over a query's heads is a sum inside the lane.  The index logits use
+// "query rows" m' = 16 t + 4q + v whose query is ri_query<G>(t, q, v).
+// ---------------------------------------------------------------------------
+constexpr int kW16 = 8;                        // waves of the 16x16 kernel
+constexpr int kT16 = kW16 * kWave;             // its threads
+
+__device__ inline f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Operand of a 16x16x32 MFMA read with the gfx950 transpose read from a
+// row-major tile of layout L: lane (q, c) gets column m0 + c and the K values
+// of rows ra .. ra+3 (slots 0..3) and rb .. rb+3 (slots 4..7), where ra and rb
+// are the lane group's row bases.
 template <class L>
-__device__ inline bf16x8 trfrag(const bf16* base, int m0, int kc, int lane) {
+__device__ inline bf16x8 tr16(const bf16* base, int m0, int ra, int rb, int lane) {
   const int jj = lane & 15;
-  const int r0 = 16 * kc + 4 * (lane >> 5) + (jj >> 2);
-  const int col = m0 + 16 * ((lane >> 4) & 1) + 4 * (jj & 3);
+  const int col = m0 + 4 * (jj & 3);
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + L::off(r0, col)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + L::off(r0 + 8, col)));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + L::off(ra + (jj >> 2), col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + L::off(rb + (jj >> 2), col)));
   const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
   bf16x8 r;
   r[0] = l4[0]; r[1] = l4[1]; r[2] = l4[2]; r[3] = l4[3];
   r[4] = h4[0]; r[5] = h4[1]; r[6] = h4[2]; r[7] = h4[3];
   return r;
 }
-// Matching B operand: slots 8kc .. 8kc+7 of a C-layout tile.
-__device__ inline bf16x8 cfrag(const f32x16& x, int kc) {
+// B operand whose K slots are rows 4q..4q+3 of tile 0 and of tile 1 of a
+// C-layout pair: the two tiles' registers as they are.
+__device__ inline bf16x8 cpair(const f32x4& a, const f32x4& b) {
   bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)x[8 * kc + i];
+  r[0] = (bf16)a[0]; r[1] = (bf16)a[1]; r[2] = (bf16)a[2]; r[3] = (bf16)a[3];
+  r[4] = (bf16)b[0]; r[5] = (bf16)b[1]; r[6] = (bf16)b[2]; r[7] = (bf16)b[3];
   return r;
 }
-__device__ inline f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ inline bf16x4 pack4(float a, float b, float c, float d) {
-  bf16x4 r;
-  r[0] = (bf16)a; r[1] = (bf16)b; r[2] = (bf16)c; r[3] = (bf16)d;
-  return r;
-}
-// x of lane l % 32 (lo) and of lane l % 32 + 32 (hi), in every lane.
-__device__ inline void halves(float x, float* lo, float* hi) {
-  const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  *lo = __uint_as_float(v[0]);
-  *hi = __uint_as_float(v[1]);
-}
-
-// Mean over the G heads of each query of a 32-row C-layout tile whose row
-// q G + e is head e of query q, returned in the C layout of a tile whose rows
-// are the queries (slot v of half hf holds query c_row(v, hf)); slots that hold
-// no query of the step are left 0.
+// Step row of tile t, lane group q, slot v -> R (query R / G, head R % G).
+__device__ inline int row_r(int t, int q, int v) { return 8 * q + 4 * t + v; }
+// Query (within the step) of query row m' = 16 t + 4 q + v, or -1.
 template <int G>
-__device__ inline f32x16 head_mean(const f32x16& p, int hf) {
-  f32x16 r = zero16();
+__device__ inline int ri_query(int t, int q, int v) {
+  if constexpr (G == 1) return 8 * q + 4 * t + v;
+  else if constexpr (G <= 8) return (t == 0 && v < 8 / G) ? q * (8 / G) + v : -1;
+  else return (t == 0 && v == 0 && (q & 1) == 0) ? q / 2 : -1;
+}
+// Teacher: mean of P over each query's heads, at the query rows' C layout.
+template <int G>
+__device__ inline void head_mean16(const f32x4* p, f32x4* pb) {
   constexpr float inv = 1.0f / G;
   if constexpr (G == 1) {
-    r = p;
-  } else if constexpr (G >= 8) {
-    // rows qG .. qG+G-1: slots [q G/2, (q+1) G/2) of both halves
-    constexpr int H2 = G / 2;
+    pb[0] = p[0];
+    pb[1] = p[1];
+  } else if constexpr (G == 2) {
 #pragma unroll
-    for (int q = 0; q < 32 / G; ++q) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < H2; ++e) s += p[q * H2 + e];
-      float lo, hi;
-      halves(s, &lo, &hi);
-      r[q] = (lo + hi) * inv;
-    }
+    for (int v = 0; v < 4; ++v) pb[0][v] = (p[v >> 1][2 * (v & 1)] + p[v >> 1][2 * (v & 1) + 1]) * inv;
   } else if constexpr (G == 4) {
-    // slots 4gi .. 4gi+3 of half h: query 2gi + h
-    float x0[4], x1[4];
+    pb[0] = zero4();
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) halves(p[4 * gi] + p[4 * gi + 1] + p[4 * gi + 2] + p[4 * gi + 3], &x0[gi], &x1[gi]);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {   // query 4 hf + v
-      const float* x = (v & 1) ? x1 : x0;
-      r[v] = (hf ? x[2 + (v >> 1)] : x[v >> 1]) * inv;
-    }
+    for (int v = 0; v < 2; ++v) pb[0][v] = (p[v][0] + p[v][1] + p[v][2] + p[v][3]) * inv;
   } else {
-    static_assert(G == 2, "group size");
-    // slots 4gi + 2k, 4gi + 2k + 1 of half h: query 4gi + 2h + k
-    float y0[4][2], y1[4][2];
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-        halves(p[4 * gi + 2 * k2] + p[4 * gi + 2 * k2 + 1], &y0[gi][k2], &y1[gi][k2]);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {   // query 8 (v / 4) + 4 hf + v % 4
-      const int g0 = 2 * (v >> 2);
-      const float a = ((v >> 1) & 1) ? y1[g0][v & 1] : y0[g0][v & 1];
-      const float c = ((v >> 1) & 1) ? y1[g0 + 1][v & 1] : y0[g0 + 1][v & 1];
-      r[v] = (hf ? c : a) * inv;
-    }
+    float s = p[0][0] + p[0][1] + p[0][2] + p[0][3] + p[1][0] + p[1][1] + p[1][2] + p[1][3];
+    if constexpr (G == 16) s += __shfl_xor(s, 16);
+    pb[0] = zero4();
+    pb[0][0] = s * inv;
   }
-  return r;
 }
 
-// ---------------------------------------------------------------------------
-// Main fused backward.  4 waves; wave w owns keys 32w..32w+31 of the block.
-// 32x32x16 MFMA tiles (C-layout: lane l holds column l % 32, rows
-// 8*(v/4) + 4*(l/32) + v%4 in slot v; A/B operands: lane l holds row/column
-// l % 32 and k = 8*(l/32) + i).  Per step of 32 (query, head) rows:
-//   S = Q K_w^T, dP = dO V_w^T, r = q_idx K_idx,w^T  (A and B from LDS tiles)
-//   P, dS; the head-mean teacher pbar, p_px and dz    (lane = key, all in registers)
-//   dV_w^T += dO^T P, dK_w^T += Q^T dS, dk_idx_w^T += q_idx^T dz
-//   dS^T, dz^T -> LDS; barrier
-//   dQ[:, 32w..32w+31] = dS K and dq_idx = dz K_idx  (A and B by transpose reads of
-//                                        dS^T / dz^T and of the K / K_idx tiles)
-// The block's K, V and K_idx stay in LDS for the whole item and every MFMA
-// operand is read from LDS, which leaves the registers to the accumulators
-// and to operands fetched ahead of their MFMAs.
-// ---------------------------------------------------------------------------
+template <int D, int DIDX>
+struct Bwd16Cfg {
+  using TQ = Tile16Of<D>;                  // Q, dO, K, V tiles
+  using TI = Pad<DIDX + 8>;                // q_idx, K_idx tiles
+  using TS = Pad<32 + 16>;                 // dS^T, dz^T: one row of 32 step rows per key; a 96-byte
+                                           // pitch keeps the transpose reads of 8 rows conflict-free
+  static constexpr int PQ = TQ::pitch, PQI = TI::pitch, PST = TS::pitch;
+  static constexpr size_t OFF_QS = 0;                                    // Q        [32][PQ]
+  static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;        // dO       [32][PQ]
+  static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;       // q_idx    [32][PQI]
+  static constexpr size_t OFF_DST = OFF_QIS + (size_t)32 * PQI * 2;      // dS^T     [128][PST]
+  static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     [128][PST]
+  static constexpr size_t OFF_TAB = OFF_DZT + (size_t)kBlock * PST * 2;  // 2 x kNumTabs x [32]
+  static constexpr size_t OFF_KS = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K  [128][PQ]
+  static constexpr size_t OFF_VS = OFF_KS + (size_t)kBlock * PQ * 2;     // V      [128][PQ]
+  static constexpr size_t OFF_KIS = OFF_VS + (size_t)kBlock * PQ * 2;    // K_idx  [128][PQI]
+  static constexpr size_t OFF_QL = OFF_KIS + (size_t)kBlock * PQI * 2;   // item queries: (t << 6) | slot
+  static constexpr size_t LDS = OFF_QL + (size_t)(kBlock + kBigItem) * 4;
+  // The flush at the end of an item reuses [OFF_KS, OFF_QL) as 8 x [16][D + 4] fp32.
+  static_assert(OFF_QL - OFF_KS >= (size_t)kW16 * 16 * (D + 4) * 4, "flush scratch");
+  static_assert(LDS <= 160 * 1024, "LDS of one CU");
+};
+
 template <int D, int DIDX, int G, bool EXTRA>
-__global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
+__global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dv,
     const bf16* __restrict__ q_idx, const bf16* __restrict__ k_idx, const float* __restrict__ lse_idx,
@@ -460,28 +419,29 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
     const int32_t* __restrict__ rows, const int32_t* __restrict__ tiles, float* __restrict__ dq_acc,
     float* __restrict__ dk_acc, float* __restrict__ dv_acc, float* __restrict__ dq_idx,
     float* __restrict__ dk_idx, float* __restrict__ dscore, float* __restrict__ kl, int N, int H_kv, int topk,
-    int causal, int nblk, int nsb, int n_lists, float scale, float scale_idx, float lam) {
-  using C = BwdCfg<D, DIDX>;
-  constexpr int KS = D / 16;        // 16-wide k-steps over d
-  constexpr int KSI = DIDX / 16;    // 16-wide k-steps over d_idx
-  constexpr int DT = D / 32;        // 32-wide d tiles
-  constexpr int DTI = DIDX / 32;    // 32-wide d_idx tiles
+    int causal, int nblk, int nsb, int n_lists, float scale, float scale_idx, float lam, int n_qrows,
+    int n_grows) {
+  using C = Bwd16Cfg<D, DIDX>;
+  constexpr int KS = D / 32;        // 32-wide k-steps over d
+  constexpr int KSI = DIDX / 32;    // 32-wide k-steps over d_idx
+  constexpr int DT = D / 16;        // 16-wide d tiles
+  constexpr int DTI = DIDX / 16;    // 16-wide d_idx tiles
   constexpr int TQ = 32 / G;        // queries per 32-row step
-  constexpr int KCQ = TQ > 16 ? 2 : 1;                     // 16-query chunks holding real queries
-  constexpr int NVQ = TQ <= 8 ? 4 : (TQ <= 16 ? 8 : 16);   // slots that can hold a query < TQ
+  constexpr int NTQ = G == 1 ? 2 : 1;                       // query-row tiles
   constexpr int CPR = D / 8;        // 16-byte chunks per Q / dO row
   constexpr int CPRI = DIDX / 8;    // 16-byte chunks per q_idx row
-  constexpr int LDM = 32 * CPR / kMainThreads;              // Q (and dO) chunks per thread
   constexpr int NT = kNumTabs * 32;
-  static_assert(32 * CPR % kMainThreads == 0, "tile split");
-  static_assert(32 * CPRI <= kMainThreads, "q_idx tile split");
-  static_assert(DT <= kBwdWaves, "one dQ column tile per wave");
+  // dQ: column tile w % DT over the key part w / DT (of KPQ parts); dq_idx likewise.
+  constexpr int KPQ = kW16 / DT;    // 1 (d = 128) or 2 (d = 64) parts of the 128 keys
+  constexpr int KPI = kW16 / DTI;   // 2 (d_idx = 64) or 4 (d_idx = 32)
+  static_assert(kW16 % DT == 0 && kW16 % DTI == 0, "wave split");
+  static_assert(32 * CPR <= kT16 && 32 * CPRI <= kT16, "one tile chunk per thread");
   extern __shared__ __align__(16) char smem[];
   bf16* Qs = reinterpret_cast<bf16*>(smem + C::OFF_QS);
   bf16* dOs = reinterpret_cast<bf16*>(smem + C::OFF_DOS);
   bf16* QIs = reinterpret_cast<bf16*>(smem + C::OFF_QIS);
   bf16* dSt = reinterpret_cast<bf16*>(smem + C::OFF_DST);
-  bf16* dZt2 = reinterpret_cast<bf16*>(smem + C::OFF_DZT);   // dz^T of steps of either parity
+  bf16* dZt = reinterpret_cast<bf16*>(smem + C::OFF_DZT);
   int* tabs = reinterpret_cast<int*>(smem + C::OFF_TAB);
   bf16* Ks = reinterpret_cast<bf16*>(smem + C::OFF_KS);
   bf16* Vs = reinterpret_cast<bf16*>(smem + C::OFF_VS);
@@ -491,203 +451,171 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
   BigItem it;
   if (!decode_big_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, &it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 31, hf = lane >> 5;
+  const int c = lane & 15, lq = lane >> 4;            // C layout: column c, rows 4 lq + v
   const int H_q = H_kv * G;
   const int b = it.b, g = it.g, j = it.j;
-  const int key = 32 * wave + n;                      // this lane's key inside the block
+  const int key = 16 * wave + c;                      // this lane's key inside the block
   const int u = j * kBlock + key;
   const size_t blk_row0 = ((size_t)b * N + (size_t)j * kBlock) * H_kv + g;   // key 0 of the block
   const int nq = it.n_own + it.ne;
   const bool want_slot = EXTRA && dscore != nullptr;
 
-  // The item's queries in LDS, so that the step loop needs no dependent
-  // global load (the vector-memory counter is in order: a wait on a
-  // dependent load would also wait for the previous step's atomics).
-  for (int qi = threadIdx.x; qi < nq; qi += kMainThreads) {
+  for (int qi = threadIdx.x; qi < nq; qi += kT16) {
     int slot;
     const int t = big_query(it, qi, block_idx, N, H_kv, topk, want_slot, &slot);
     qlist[qi] = t < 0 ? -1 : ((t << 6) | slot);
   }
-  // K, V and K_idx of the block in LDS, row-major (one row per key).
-  for (int c = threadIdx.x; c < kBlock * CPR; c += kMainThreads) {
-    const int kk = c / CPR, col = (c % CPR) * 8;
+  for (int cc = threadIdx.x; cc < kBlock * CPR; cc += kT16) {
+    const int kk = cc / CPR, col = (cc % CPR) * 8;
     const size_t row = blk_row0 + (size_t)kk * H_kv;
     *reinterpret_cast<bf16x8*>(Ks + C::TQ::off(kk, col)) = *reinterpret_cast<const bf16x8*>(k + row * D + col);
     *reinterpret_cast<bf16x8*>(Vs + C::TQ::off(kk, col)) = *reinterpret_cast<const bf16x8*>(v + row * D + col);
   }
-  for (int c = threadIdx.x; c < kBlock * CPRI; c += kMainThreads) {
-    const int kk = c / CPRI, col = (c % CPRI) * 8;
+  for (int cc = threadIdx.x; cc < kBlock * CPRI; cc += kT16) {
+    const int kk = cc / CPRI, col = (cc % CPRI) * 8;
     *reinterpret_cast<bf16x8*>(KIs + C::TI::off(kk, col)) =
         *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
   }
-  const bool has_q = DT == kBwdWaves || wave < DT;   // the wave owns dQ columns 32w..32w+31
-  // dq_idx: output tile wave % DTI, over the 16-key chunks
-  // [kpart * KCW, (kpart + 1) * KCW), so every wave issues the same atomics.
-  constexpr int KPARTS = kBwdWaves / DTI;
-  constexpr int KCW = 8 / KPARTS;
-  const int itile = wave % DTI, kpart = wave / DTI;
-  const int qcol = 32 * wave + n;                     // dQ column (wave < DT)
+  const int qct = wave % DT, qkp = wave / DT;         // dQ column tile and key part
+  const int ict = wave % DTI, ikp = wave / DTI;       // dq_idx column tile and key part
 
-  f32x16 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
+  f32x4 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
 #pragma unroll
   for (int i = 0; i < DT; ++i) {
-    acc_dv[i] = zero16();
-    acc_dk[i] = zero16();
+    acc_dv[i] = zero4();
+    acc_dk[i] = zero4();
   }
 #pragma unroll
-  for (int i = 0; i < DTI; ++i) acc_dki[i] = zero16();
+  for (int i = 0; i < DTI; ++i) acc_dki[i] = zero4();
   __syncthreads();   // item query list and the K, V, K_idx tiles ready
 
-  // Per-thread share of a step, loaded into registers one step ahead: LDM
-  // 16-byte chunks of Q and dO (with LSE, D, cut-off and id of the rows whose
-  // first chunk it holds), one chunk of q_idx, and - for threads < TQ - the
-  // step's query table entry.  The loads of step st + 1 are issued at the top
-  // of step st, before its atomics; the vector-memory counter completes in
-  // order, so the wait for them at the end of the step covers nothing issued
-  // later, as long as every memory operation in between is unconditional and
-  // can be counted.  The query-list entries the loads need are read from LDS
-  // one step before they are issued (pk_*).
+  // Per-thread share of a step, loaded one step ahead: one 16-byte chunk of
+  // Q and of dO (thread < 32 CPR) with the row's statistics when the chunk is
+  // the row's first, one chunk of q_idx (thread < 32 CPRI), and the query-row
+  // table entry (thread < 32).
+  const int tx = threadIdx.x;
+  const bool ld_row = tx < 32 * CPR;
+  const int ld_m = (tx / CPR) & 31, ld_col = (tx % CPR) * 8;
+  const int ld_rr = row_r(ld_m >> 4, (ld_m >> 2) & 3, ld_m & 3);   // R of the thread's row
+  const bool ld_qi = tx < 32 * CPRI;
+  const int ld_mi = (tx / CPRI) & 31, ld_qcol = (tx % CPRI) * 8;
+  const int ld_qq = ri_query<G>(ld_mi >> 4, (ld_mi >> 2) & 3, ld_mi & 3);
+  const int mq = tx & 31;
+  const int mq_q = ri_query<G>(mq >> 4, (mq >> 2) & 3, mq & 3);
   struct Pre {
-    bf16x8 q[LDM], d[LDM], qi;
-    float lse[LDM], rd[LDM], qlse;
-    int t[LDM], cut[LDM], id[LDM], qt, qslot, qcut, qid;
+    bf16x8 q, d, qi;
+    float lse, rd, qlse;
+    int t, cut, id, qt, qslot, qcut, qid;
   };
   Pre pre;
-  int pk_e[LDM], pk_qi = -1, pk_qt = -1;
-  const int ld_col = (threadIdx.x % CPR) * 8;
-  const int ld_qr = threadIdx.x / CPRI, ld_qcol = (threadIdx.x % CPRI) * 8;
-  const bool ld_idx = threadIdx.x < 32 * CPRI;
-  const int tx = threadIdx.x & 31;
+  int pk_e = -1, pk_qi = -1, pk_qt = -1;
   auto entry = [&](int qi) { return qi < nq ? qlist[qi] : -1; };
   auto cutoff = [&](int qi, int t) { return t < 0 ? -1 : ((qi < it.n_own && causal) ? t : 0x7fffffff); };
   auto peek = [&](int st) {
-#pragma unroll
-    for (int c = 0; c < LDM; ++c) pk_e[c] = entry((32 * st + (threadIdx.x + c * kMainThreads) / CPR) / G);
-    pk_qi = ld_qr < TQ ? entry(st * TQ + ld_qr) : -1;
-    pk_qt = tx < TQ ? entry(st * TQ + tx) : -1;
+    pk_e = ld_row ? entry(st * TQ + ld_rr / G) : -1;
+    pk_qi = (ld_qi && ld_qq >= 0) ? entry(st * TQ + ld_qq) : -1;
+    pk_qt = (tx < 32 && mq_q >= 0) ? entry(st * TQ + mq_q) : -1;
   };
-  // Every load below is unconditional (clamped to a valid row; past the end
-  // of the item it re-reads valid rows, unused) so that the compiler can count
-  // the memory operations exactly.
-  auto load_step = [&](int st, Pre& x) {
-#pragma unroll
-    for (int c = 0; c < LDM; ++c) {
-      const int r = (threadIdx.x + c * kMainThreads) / CPR;
-      const int t = pk_e[c] < 0 ? -1 : (pk_e[c] >> 6);
-      x.t[c] = t;
-      x.cut[c] = cutoff((32 * st + r) / G, t);
-      const size_t qrow = ((size_t)b * N + (t < 0 ? 0 : t)) * H_q + g * G + r % G;
-      x.id[c] = t < 0 ? -1 : (int)qrow;
-      x.q[c] = *reinterpret_cast<const bf16x8*>(q + qrow * D + ld_col);
-      x.d[c] = *reinterpret_cast<const bf16x8*>(dO + qrow * D + ld_col);
-      x.lse[c] = lse[qrow];
-      x.rd[c] = Dv[qrow];
+  // Unconditional loads (clamped to a valid row): the compiler counts them.
+  auto load_step = [&](int st) {
+    {
+      const int t = pk_e < 0 ? -1 : (pk_e >> 6);
+      pre.t = t;
+      pre.cut = cutoff(st * TQ + ld_rr / G, t);
+      const size_t qrow = ((size_t)b * N + (t < 0 ? 0 : t)) * H_q + g * G + ld_rr % G;
+      pre.id = t < 0 ? -1 : (int)qrow;
+      pre.q = *reinterpret_cast<const bf16x8*>(q + qrow * D + ld_col);
+      pre.d = *reinterpret_cast<const bf16x8*>(dO + qrow * D + ld_col);
+      pre.lse = lse[qrow];
+      pre.rd = Dv[qrow];
     }
     {
       const int tq = pk_qi < 0 ? -1 : (pk_qi >> 6);
-      x.qi = *reinterpret_cast<const bf16x8*>(q_idx + (((size_t)b * N + (tq < 0 ? 0 : tq)) * H_kv + g) * DIDX +
-                                              ld_qcol);
-      if (tq < 0) x.qi = bf16x8{};
+      pre.qi = *reinterpret_cast<const bf16x8*>(q_idx + (((size_t)b * N + (tq < 0 ? 0 : tq)) * H_kv + g) * DIDX +
+                                                ld_qcol);
+      if (tq < 0) pre.qi = bf16x8{};
     }
     {
-      x.qt = pk_qt < 0 ? -1 : (pk_qt >> 6);
-      x.qslot = pk_qt < 0 ? 0 : (pk_qt & 63);
-      x.qcut = cutoff(st * TQ + tx, x.qt);
-      const size_t qrow = ((size_t)b * N + (x.qt < 0 ? 0 : x.qt)) * H_kv + g;
-      x.qid = x.qt < 0 ? -1 : (int)qrow;
-      x.qlse = lse_idx[qrow];
+      pre.qt = pk_qt < 0 ? -1 : (pk_qt >> 6);
+      pre.qslot = pk_qt < 0 ? 0 : (pk_qt & 63);
+      pre.qcut = cutoff(st * TQ + (mq_q < 0 ? 0 : mq_q), pre.qt);
+      const size_t qrow = ((size_t)b * N + (pre.qt < 0 ? 0 : pre.qt)) * H_kv + g;
+      pre.qid = pre.qt < 0 ? -1 : (int)qrow;
+      pre.qlse = lse_idx[qrow];
     }
   };
-  // Store a step's prefetched registers into its LDS tiles and tables.
-  auto store_step = [&](int st, const Pre& x) {
+  auto store_step = [&](int st) {
     int* tb = tabs + (st & 1) * NT;
     float* tf = reinterpret_cast<float*>(tb);
-#pragma unroll
-    for (int c = 0; c < LDM; ++c) {
-      const int r = (threadIdx.x + c * kMainThreads) / CPR;
-      *reinterpret_cast<bf16x8*>(Qs + C::TQ::off(r, ld_col)) = x.q[c];
-      *reinterpret_cast<bf16x8*>(dOs + C::TQ::off(r, ld_col)) = x.d[c];
+    if (ld_row) {
+      *reinterpret_cast<bf16x8*>(Qs + C::TQ::off(ld_m, ld_col)) = pre.q;
+      *reinterpret_cast<bf16x8*>(dOs + C::TQ::off(ld_m, ld_col)) = pre.d;
       if (ld_col == 0) {
-        tb[kRowT * 32 + r] = x.t[c];
-        tb[kRowCut * 32 + r] = x.cut[c];
-        tf[kRowLse * 32 + r] = x.lse[c] * kLog2e;
-        tf[kRowD * 32 + r] = x.rd[c];
-        tb[kRowId * 32 + r] = x.id[c];
+        tb[kRowT * 32 + ld_m] = pre.t;
+        tb[kRowCut * 32 + ld_m] = pre.cut;
+        tf[kRowLse * 32 + ld_m] = pre.lse * kLog2e;
+        tf[kRowD * 32 + ld_m] = pre.rd;
+        tb[kRowId * 32 + ld_m] = pre.id;
       }
     }
-    if (ld_idx) *reinterpret_cast<bf16x8*>(QIs + C::TI::off(ld_qr, ld_qcol)) = x.qi;
-    if (threadIdx.x < 32) {
-      tb[kQryT * 32 + tx] = x.qt;
-      tb[kQrySlot * 32 + tx] = x.qslot;
-      tb[kQryCut * 32 + tx] = x.qcut;
-      tf[kQryLse * 32 + tx] = x.qlse * kLog2e;
+    if (ld_qi) *reinterpret_cast<bf16x8*>(QIs + C::TI::off(ld_mi, ld_qcol)) = pre.qi;
+    if (tx < 32) {
+      tb[kQryT * 32 + tx] = pre.qt;
+      tb[kQrySlot * 32 + tx] = pre.qslot;
+      tb[kQryCut * 32 + tx] = pre.qcut;
+      tf[kQryLse * 32 + tx] = pre.qlse * kLog2e;
       tf[kQryKl * 32 + tx] = 0.f;
-      tb[kQryId * 32 + tx] = x.qid;
+      tb[kQryId * 32 + tx] = pre.qid;
     }
   };
 
   const float c_s = scale * kLog2e;
   const float c_i = scale_idx * kLog2e;
   const int n_steps = (nq * G + 31) / 32;
-
-  // dq_idx[queries, tile] = dz K_idx over this wave's share of the keys
-  // (lane = d_idx column, slots = queries), for step st.  It runs at the top
-  // of step st + 1, before that step's loads are issued: its atomics are
-  // conditional, so the compiler cannot count them, and there they sit
-  // behind no load that has to be waited for.  dz^T is double buffered for it.
-  auto dq_idx_step = [&](int st) {
-    const int* tb = tabs + (st & 1) * NT;
-    const bf16* dZt = dZt2 + (st & 1) * kBlock * C::PST;
-    f32x16 o = zero16();
-#pragma unroll
-    for (int kc = 0; kc < KCW; ++kc) {
-      const int kq = kpart * KCW + kc;
-      o = mma32(trfrag<typename C::TS>(dZt, 0, kq, lane), trfrag<typename C::TI>(KIs, 32 * itile, kq, lane), o);
-    }
-    const int qid0 = max(tb[kQryId * 32], 0);
-#pragma unroll
-    for (int vv = 0; vv < NVQ; ++vv) {
-      const int qr = c_row(vv, lane);
-      if (qr < TQ) {
-        const int id = tb[kQryId * 32 + qr];
-        atomicAdd(dq_idx + (size_t)(id >= 0 ? id : qid0) * DIDX + 32 * itile + n, id >= 0 ? o[vv] : 0.f);
-      }
-    }
-  };
-
   peek(0);
-  load_step(0, pre);
-  store_step(0, pre);
+  load_step(0);
+  store_step(0);
   peek(1);
 #pragma unroll 1
   for (int st = 0; st < n_steps; ++st) {
     asm volatile("" ::: "memory");
     const int* tb = tabs + (st & 1) * NT;
     const float* tf = reinterpret_cast<const float*>(tb);
-    __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T consumed
-    if (st > 0) dq_idx_step(st - 1);
-    load_step(st + 1, pre);
+    __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T / dz^T consumed
+    load_step(st + 1);
     peek(st + 2);
 
-    // S, dP, index logits (lane = key, slots = rows / queries).
-    f32x16 s = zero16(), dp = zero16(), ri = zero16();
+    // S, dP (two row tiles) and the index logits (NTQ query-row tiles): lane
+    // = key, slots = rows.
+    f32x4 s[2], dp[2], ri[NTQ];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // S: A = Q rows (lane = row n), B = K rows (lane = key); dP likewise.
-      s = mma32(*reinterpret_cast<const bf16x8*>(Qs + C::TQ::off(n, 16 * ks + 8 * hf)),
-                *reinterpret_cast<const bf16x8*>(Ks + C::TQ::off(key, 16 * ks + 8 * hf)), s);
-      dp = mma32(*reinterpret_cast<const bf16x8*>(dOs + C::TQ::off(n, 16 * ks + 8 * hf)),
-                 *reinterpret_cast<const bf16x8*>(Vs + C::TQ::off(key, 16 * ks + 8 * hf)), dp);
+    for (int t = 0; t < 2; ++t) {
+      s[t] = zero4();
+      dp[t] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int col = 32 * ks + 8 * lq;
+        s[t] = mma16(*reinterpret_cast<const bf16x8*>(Qs + C::TQ::off(16 * t + c, col)),
+                     *reinterpret_cast<const bf16x8*>(Ks + C::TQ::off(key, col)), s[t]);
+        dp[t] = mma16(*reinterpret_cast<const bf16x8*>(dOs + C::TQ::off(16 * t + c, col)),
+                      *reinterpret_cast<const bf16x8*>(Vs + C::TQ::off(key, col)), dp[t]);
+      }
     }
 #pragma unroll
-    for (int ks = 0; ks < KSI; ++ks)
-      ri = mma32(*reinterpret_cast<const bf16x8*>(QIs + C::TI::off(n, 16 * ks + 8 * hf)),
-                 *reinterpret_cast<const bf16x8*>(KIs + C::TI::off(key, 16 * ks + 8 * hf)), ri);
-    // P, dS; dS^T to LDS.
-    f32x16 p, ds;
+    for (int t = 0; t < NTQ; ++t) {
+      ri[t] = zero4();
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int r4 = 8 * grp + 4 * hf;                 // rows r4 .. r4+3 = slots 4grp .. 4grp+3
+      for (int ks = 0; ks < KSI; ++ks) {
+        const int col = 32 * ks + 8 * lq;
+        ri[t] = mma16(*reinterpret_cast<const bf16x8*>(QIs + C::TI::off(16 * t + c, col)),
+                      *reinterpret_cast<const bf16x8*>(KIs + C::TI::off(key, col)), ri[t]);
+      }
+    }
+    // P, dS; dS^T to LDS (rows 16 t + 4 lq .. +3 of this lane's key).
+    f32x4 p[2], ds[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r4 = 16 * t + 4 * lq;
       const int4 cut = *reinterpret_cast<const int4*>(tb + kRowCut * 32 + r4);
       const float4 l2 = *reinterpret_cast<const float4*>(tf + kRowLse * 32 + r4);
       const float4 dd = *reinterpret_cast<const float4*>(tf + kRowD * 32 + r4);
@@ -696,127 +624,136 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_main_kernel(
       const float dds[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int vv = 4 * grp + e;
-        const float pv = u <= cuts[e] ? __builtin_amdgcn_exp2f(s[vv] * c_s - l2s[e]) : 0.f;
-        p[vv] = pv;
-        ds[vv] = pv * (dp[vv] - dds[e]) * scale;
+        const float pv = u <= cuts[e] ? __builtin_amdgcn_exp2f(s[t][e] * c_s - l2s[e]) : 0.f;
+        p[t][e] = pv;
+        ds[t][e] = pv * (dp[t][e] - dds[e]) * scale;
       }
-      *reinterpret_cast<bf16x4*>(dSt + key * C::PST + r4) =
-          pack4(ds[4 * grp], ds[4 * grp + 1], ds[4 * grp + 2], ds[4 * grp + 3]);
+      *reinterpret_cast<bf16x4*>(dSt + key * C::PST + r4) = pack4(ds[t][0], ds[t][1], ds[t][2], ds[t][3]);
     }
-    // Index branch on the query slots: teacher pbar (mean of P over the
-    // query's heads), p_px, dz = lam (p_px - pbar); dz^T to LDS.
-    const f32x16 pb = head_mean<G>(p, hf);
-    f32x16 dz = zero16();
+    // Teacher, p_px, dz on the query rows; dz^T to LDS.
+    f32x4 pb[NTQ], dz[NTQ];
+    head_mean16<G>(p, pb);
 #pragma unroll
-    for (int gq = 0; gq < NVQ / 4; ++gq) {
-      const int r4 = 8 * gq + 4 * hf;                  // queries r4 .. r4+3 = slots 4gq .. 4gq+3
+    for (int t = 0; t < NTQ; ++t) {
+      const int r4 = 16 * t + 4 * lq;
       const int4 qc = *reinterpret_cast<const int4*>(tb + kQryCut * 32 + r4);
       const float4 ql = *reinterpret_cast<const float4*>(tf + kQryLse * 32 + r4);
       const int qcs[4] = {qc.x, qc.y, qc.z, qc.w};
       const float qls[4] = {ql.x, ql.y, ql.z, ql.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int vv = 4 * gq + e;
-        const float lz = ri[vv] * c_i - qls[e];       // log2 p_px
+        const float lz = ri[t][e] * c_i - qls[e];     // log2 p_px
         const bool vis = u <= qcs[e];                  // -1 for rows that hold no query
-        dz[vv] = vis ? lam * (__builtin_amdgcn_exp2f(lz) - pb[vv]) : 0.f;
+        dz[t][e] = vis ? lam * (__builtin_amdgcn_exp2f(lz) - pb[t][e]) : 0.f;
         if (EXTRA && dscore != nullptr && vis) {
-          const int qr = r4 + e;
-          dscore[((((size_t)b * N + tb[kQryT * 32 + qr]) * H_kv + g) * topk + tb[kQrySlot * 32 + qr]) * kBlock +
-                 key] = dz[vv];
+          const int tq = tb[kQryT * 32 + r4 + e], sl = tb[kQrySlot * 32 + r4 + e];
+          if ((unsigned)tq < (unsigned)N && (unsigned)sl < (unsigned)topk)
+            dscore[((((size_t)b * N + tq) * H_kv + g) * topk + sl) * kBlock + key] = dz[t][e];
         }
         if (EXTRA && kl != nullptr) {
-          float klv = (vis && pb[vv] > 0.f) ? pb[vv] * (logf(pb[vv]) - lz * kLn2) : 0.f;
+          float klv = (vis && pb[t][e] > 0.f) ? pb[t][e] * (logf(pb[t][e]) - lz * kLn2) : 0.f;
 #pragma unroll
-          for (int off = 16; off > 0; off >>= 1) klv += __shfl_xor(klv, off);   // over the half-wave's 32 keys
-          if (n == 0 && r4 + e < TQ) atomicAdd(reinterpret_cast<float*>(tabs + (st & 1) * NT) + kQryKl * 32 + r4 + e, klv);
+          for (int off = 8; off > 0; off >>= 1) klv += __shfl_xor(klv, off);   // over the lane group's 16 keys
+          if (c == 0 && qcs[e] >= 0)
+            atomicAdd(reinterpret_cast<float*>(tabs + (st & 1) * NT) + kQryKl * 32 + r4 + e, klv);
         }
       }
-      if (r4 < TQ)
-        *reinterpret_cast<bf16x4*>(dZt2 + (st & 1) * kBlock * C::PST + key * C::PST + r4) =
-            pack4(dz[4 * gq] * scale_idx, dz[4 * gq + 1] * scale_idx, dz[4 * gq + 2] * scale_idx,
-                  dz[4 * gq + 3] * scale_idx);
+      *reinterpret_cast<bf16x4*>(dZt + key * C::PST + r4) =
+          pack4(dz[t][0] * scale_idx, dz[t][1] * scale_idx, dz[t][2] * scale_idx, dz[t][3] * scale_idx);
     }
-    // dV^T += dO^T P, dK^T += Q^T dS, dk_idx^T += q_idx^T dz.
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const bf16x8 pbf = cfrag(p, kc), sbf = cfrag(ds, kc);
+    // dV^T += dO^T P, dK^T += Q^T dS (K = the 32 rows, in the order of the
+    // two tiles' slots), dk_idx^T += q_idx^T dz.
+    {
+      const bf16x8 pbf = cpair(p[0], p[1]), sbf = cpair(ds[0], ds[1]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        acc_dv[dt] = mma32(trfrag<typename C::TQ>(dOs, 32 * dt, kc, lane), pbf, acc_dv[dt]);
-        acc_dk[dt] = mma32(trfrag<typename C::TQ>(Qs, 32 * dt, kc, lane), sbf, acc_dk[dt]);
+        acc_dv[dt] = mma16(tr16<typename C::TQ>(dOs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), pbf, acc_dv[dt]);
+        acc_dk[dt] = mma16(tr16<typename C::TQ>(Qs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), sbf, acc_dk[dt]);
       }
-    }
-    {
-      f32x16 zs;
+      const bf16x8 zb = cpair(dz[0] * scale_idx, NTQ == 2 ? dz[NTQ - 1] * scale_idx : zero4());
 #pragma unroll
-      for (int vv = 0; vv < 16; ++vv) zs[vv] = dz[vv] * scale_idx;
-#pragma unroll
-      for (int kc = 0; kc < KCQ; ++kc) {
-        const bf16x8 zb = cfrag(zs, kc);
-#pragma unroll
-        for (int dt = 0; dt < DTI; ++dt)
-          acc_dki[dt] = mma32(trfrag<typename C::TI>(QIs, 32 * dt, kc, lane), zb, acc_dki[dt]);
-      }
+      for (int dt = 0; dt < DTI; ++dt)
+        acc_dki[dt] = mma16(tr16<typename C::TI>(QIs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), zb, acc_dki[dt]);
     }
     __syncthreads();   // dS^T, dz^T and the KL partials complete
 
-    // dQ[rows, wave's 32 columns] = dS K (this wave's share of the keys): lane
-    // = output column, slots = rows, so each atomic instruction covers 32
-    // consecutive floats of one row per half-wave.  A row without a query adds
-    // 0 at the step's first row (always a real one) instead of branching, so
-    // the number of memory operations after the loads is fixed and the wait
-    // for them at the end of the step covers none of these atomics.
-    if (has_q) {
-      f32x16 o = zero16();
+    // dQ[rows, column tile qct] = dS K over key part qkp: lane = column,
+    // slots = rows, one atomic instruction per (tile, slot) covering 4 rows x
+    // 16 consecutive floats.  A row without a query adds 0 at the step's first
+    // row (always a real one), so the atomics are unconditional.  Every id is
+    // checked against the row count before it becomes an address.
+    {
+      f32x4 o[2];
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        o = mma32(trfrag<typename C::TS>(dSt, 0, kc, lane), trfrag<typename C::TQ>(Ks, 32 * wave, kc, lane), o);
-      const int id0 = max(tb[kRowId * 32], 0);
+      for (int t = 0; t < 2; ++t) {
+        o[t] = zero4();
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int4 id4 = *reinterpret_cast<const int4*>(tb + kRowId * 32 + 8 * grp + 4 * hf);
+        for (int ks = 0; ks < 4 / KPQ; ++ks) {
+          const int k0 = 32 * (qkp * (4 / KPQ) + ks) + 4 * lq;   // keys k0 .. k0+3, k0+16 .. k0+19
+          o[t] = mma16(tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane),
+                       tr16<typename C::TQ>(Ks, 16 * qct, k0, k0 + 16, lane), o[t]);
+        }
+      }
+      const int id0r = tb[kRowId * 32];
+      const int id0 = (unsigned)id0r < (unsigned)n_qrows ? id0r : 0;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int4 id4 = *reinterpret_cast<const int4*>(tb + kRowId * 32 + 16 * t + 4 * lq);
         const int ids[4] = {id4.x, id4.y, id4.z, id4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int vv = 4 * grp + e;
-          atomicAdd(dq_acc + (size_t)(ids[e] >= 0 ? ids[e] : id0) * D + qcol, ids[e] >= 0 ? o[vv] : 0.f);
+          const bool ok = (unsigned)ids[e] < (unsigned)n_qrows;
+          atomicAdd(dq_acc + (size_t)(ok ? ids[e] : id0) * D + 16 * qct + c, ok ? o[t][e] : 0.f);
         }
       }
     }
-    if (EXTRA && kl != nullptr && threadIdx.x < TQ && tb[kQryId * 32 + threadIdx.x] >= 0)
-      atomicAdd(&kl[tb[kQryId * 32 + threadIdx.x]], tf[kQryKl * 32 + threadIdx.x]);
-    // Step st + 1's tiles: nothing reads Qs / dOs / QIs or the other table set
-    // after the barrier above, so this can overlap the atomics.
-    store_step(st + 1, pre);
+    // dq_idx[query rows, column tile ict] = dz K_idx over key part ikp.
+    {
+      f32x4 o[NTQ];
+#pragma unroll
+      for (int t = 0; t < NTQ; ++t) {
+        o[t] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4 / KPI; ++ks) {
+          const int k0 = 32 * (ikp * (4 / KPI) + ks) + 4 * lq;
+          o[t] = mma16(tr16<typename C::TS>(dZt, 16 * t, k0, k0 + 16, lane),
+                       tr16<typename C::TI>(KIs, 16 * ict, k0, k0 + 16, lane), o[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NTQ; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ri_query<G>(t, lq, e) >= 0) {
+            const int id = tb[kQryId * 32 + 16 * t + 4 * lq + e];
+            if ((unsigned)id < (unsigned)n_grows) atomicAdd(dq_idx + (size_t)id * DIDX + 16 * ict + c, o[t][e]);
+          }
+    }
+    if (EXTRA && kl != nullptr && threadIdx.x < 32) {
+      const int id = tb[kQryId * 32 + threadIdx.x];
+      if ((unsigned)id < (unsigned)n_grows) atomicAdd(&kl[id], tf[kQryKl * 32 + threadIdx.x]);
+    }
+    store_step(st + 1);
   }
-  dq_idx_step(n_steps - 1);   // dz^T of the last step is complete (barrier before its dQ)
 
-  // Flush the block's dK, dV (group g) and dk_idx (shared by the groups)
-  // through LDS, so that each atomic instruction covers two 32-float runs of
-  // one key row instead of 32 rows.
-  float* scr = reinterpret_cast<float*>(smem + C::OFF_QS) + wave * 32 * 33;
-  auto flush = [&](const f32x16& acc, float* dst_row0, size_t row_stride) {
+  // Flush the wave's dK, dV (group g) and dk_idx (shared by the groups):
+  // C layout [d rows][16 keys] -> LDS [16 keys][d] -> atomics of whole key rows.
+  float* scr = reinterpret_cast<float*>(smem + C::OFF_KS) + wave * 16 * (D + 4);
+  auto flush = [&](const f32x4* acc, int ntile, int width, float* dst_row0, size_t row_stride) {
     __syncthreads();
+    for (int dt = 0; dt < ntile; ++dt)
 #pragma unroll
-    for (int vv = 0; vv < 16; ++vv) scr[n * 33 + c_row(vv, lane)] = acc[vv];
+      for (int e = 0; e < 4; ++e) scr[c * (D + 4) + 16 * dt + 4 * lq + e] = acc[dt][e];
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const int kr = 2 * kk + hf;                      // key row of the wave
-      atomicAdd(dst_row0 + (size_t)kr * row_stride + n, scr[kr * 33 + n]);
+    for (int i = lane; i < 16 * width; i += 64) {
+      const int kr = i / width, col = i % width;
+      atomicAdd(dst_row0 + (size_t)kr * row_stride + col, scr[kr * (D + 4) + col]);
     }
   };
-  const size_t kv0 = ((size_t)b * N + (size_t)j * kBlock + 32 * wave) * H_kv + g;   // wave's first key row
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    flush(acc_dk[dt], dk_acc + kv0 * D + 32 * dt, (size_t)H_kv * D);
-    flush(acc_dv[dt], dv_acc + kv0 * D + 32 * dt, (size_t)H_kv * D);
-  }
-#pragma unroll
-  for (int dt = 0; dt < DTI; ++dt)
-    flush(acc_dki[dt], dk_idx + ((size_t)b * N + (size_t)j * kBlock + 32 * wave) * DIDX + 32 * dt, (size_t)DIDX);
+  const size_t kv0 = ((size_t)b * N + (size_t)j * kBlock + 16 * wave) * H_kv + g;   // wave's first key row
+  flush(acc_dk, DT, D, dk_acc + kv0 * D, (size_t)H_kv * D);
+  flush(acc_dv, DT, D, dv_acc + kv0 * D, (size_t)H_kv * D);
+  flush(acc_dki, DTI, DIDX, dk_idx + ((size_t)b * N + (size_t)j * kBlock + 16 * wave) * DIDX, (size_t)DIDX);
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst,
@@ -841,20 +778,21 @@ hipError_t to_bf16(const float* src, void* dst, size_t n, hipStream_t s) {
 template <int D, int DIDX, int G>
 hipError_t run_main(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w, int grid,
                     hipStream_t s) {
-  using C = BwdCfg<D, DIDX>;
+  using C = Bwd16Cfg<D, DIDX>;
   // The optional per-score outputs get their own instantiation so that the
   // plain training path carries none of their registers.
-  auto kern = (a.dscore != nullptr || a.kl != nullptr) ? bwd_main_kernel<D, DIDX, G, true>
-                                                       : bwd_main_kernel<D, DIDX, G, false>;
+  auto kern = (a.dscore != nullptr || a.kl != nullptr) ? bwd_main16_kernel<D, DIDX, G, true>
+                                                       : bwd_main16_kernel<D, DIDX, G, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kMainThreads), C::LDS, s, static_cast<const bf16*>(a.q),
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kT16), C::LDS, s, static_cast<const bf16*>(a.q),
                      static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dO),
                      a.lse, w.D, static_cast<const bf16*>(a.q_idx), static_cast<const bf16*>(a.k_idx), w.lse_idx,
                      a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.dq_acc, w.dk_acc, w.dv_acc, a.dq_idx,
                      a.dk_idx, a.dscore, a.kl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb,
-                     P.B * P.H_kv * P.nblk, P.scale, P.scale_idx, a.kl_weight);
+                     P.B * P.H_kv * P.nblk, P.scale, P.scale_idx, a.kl_weight, P.B * P.N * P.H_q,
+                     P.B * P.N * P.H_kv);
   return hipGetLastError();
 }
 
