@@ -398,8 +398,8 @@ struct Bwd16Cfg {
   static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;        // dO       [32][PQ]
   static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;       // q_idx    [32][PQI]
   static constexpr size_t OFF_DST = OFF_QIS + (size_t)32 * PQI * 2;      // dS^T     [128][PST]
-  static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     [128][PST]
-  static constexpr size_t OFF_TAB = OFF_DZT + (size_t)kBlock * PST * 2;  // 2 x kNumTabs x [32]
+  static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     2 x [128][PST]
+  static constexpr size_t OFF_TAB = OFF_DZT + (size_t)2 * kBlock * PST * 2;   // 2 x kNumTabs x [32]
   static constexpr size_t OFF_KS = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K  [128][PQ]
   static constexpr size_t OFF_VS = OFF_KS + (size_t)kBlock * PQ * 2;     // V      [128][PQ]
   static constexpr size_t OFF_KIS = OFF_VS + (size_t)kBlock * PQ * 2;    // K_idx  [128][PQI]
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   bf16* dOs = reinterpret_cast<bf16*>(smem + C::OFF_DOS);
   bf16* QIs = reinterpret_cast<bf16*>(smem + C::OFF_QIS);
   bf16* dSt = reinterpret_cast<bf16*>(smem + C::OFF_DST);
-  bf16* dZt = reinterpret_cast<bf16*>(smem + C::OFF_DZT);
+  bf16* dZt2 = reinterpret_cast<bf16*>(smem + C::OFF_DZT);  // dz^T of steps of either parity
   int* tabs = reinterpret_cast<int*>(smem + C::OFF_TAB);
   bf16* Ks = reinterpret_cast<bf16*>(smem + C::OFF_KS);
   bf16* Vs = reinterpret_cast<bf16*>(smem + C::OFF_VS);
@@ -572,6 +572,34 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   const float c_s = scale * kLog2e;
   const float c_i = scale_idx * kLog2e;
   const int n_steps = (nq * G + 31) / 32;
+  // dq_idx[query rows, column tile ict] = dz K_idx over key part ikp, for
+  // step st.  It runs at the top of step st + 1, before that step's loads are
+  // issued: its atomics are conditional, so the compiler cannot count them, and
+  // there they sit behind no load that has to be waited for (dz^T is double
+  // buffered for it).
+  auto dq_idx_step = [&](int st) {
+    const int* tb = tabs + (st & 1) * NT;
+    const bf16* dZt = dZt2 + (st & 1) * kBlock * C::PST;
+    f32x4 o[NTQ];
+#pragma unroll
+    for (int t = 0; t < NTQ; ++t) {
+      o[t] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4 / KPI; ++ks) {
+        const int k0 = 32 * (ikp * (4 / KPI) + ks) + 4 * lq;
+        o[t] = mma16(tr16<typename C::TS>(dZt, 16 * t, k0, k0 + 16, lane),
+                     tr16<typename C::TI>(KIs, 16 * ict, k0, k0 + 16, lane), o[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NTQ; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ri_query<G>(t, lq, e) >= 0) {
+          const int id = tb[kQryId * 32 + 16 * t + 4 * lq + e];
+          if ((unsigned)id < (unsigned)n_grows) atomicAdd(dq_idx + (size_t)id * DIDX + 16 * ict + c, o[t][e]);
+        }
+  };
   peek(0);
   load_step(0);
   store_step(0);
@@ -581,7 +609,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     asm volatile("" ::: "memory");
     const int* tb = tabs + (st & 1) * NT;
     const float* tf = reinterpret_cast<const float*>(tb);
-    __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T / dz^T consumed
+    __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T / dz^T complete
+    if (st > 0) dq_idx_step(st - 1);
     load_step(st + 1);
     peek(st + 2);
 
@@ -658,7 +687,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
             atomicAdd(reinterpret_cast<float*>(tabs + (st & 1) * NT) + kQryKl * 32 + r4 + e, klv);
         }
       }
-      *reinterpret_cast<bf16x4*>(dZt + key * C::PST + r4) =
+      *reinterpret_cast<bf16x4*>(dZt2 + (st & 1) * kBlock * C::PST + key * C::PST + r4) =
           pack4(dz[t][0] * scale_idx, dz[t][1] * scale_idx, dz[t][2] * scale_idx, dz[t][3] * scale_idx);
     }
     // dV^T += dO^T P, dK^T += Q^T dS (K = the 32 rows, in the order of the
@@ -707,34 +736,13 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         }
       }
     }
-    // dq_idx[query rows, column tile ict] = dz K_idx over key part ikp.
-    {
-      f32x4 o[NTQ];
-#pragma unroll
-      for (int t = 0; t < NTQ; ++t) {
-        o[t] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < 4 / KPI; ++ks) {
-          const int k0 = 32 * (ikp * (4 / KPI) + ks) + 4 * lq;
-          o[t] = mma16(tr16<typename C::TS>(dZt, 16 * t, k0, k0 + 16, lane),
-                       tr16<typename C::TI>(KIs, 16 * ict, k0, k0 + 16, lane), o[t]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < NTQ; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (ri_query<G>(t, lq, e) >= 0) {
-            const int id = tb[kQryId * 32 + 16 * t + 4 * lq + e];
-            if ((unsigned)id < (unsigned)n_grows) atomicAdd(dq_idx + (size_t)id * DIDX + 16 * ict + c, o[t][e]);
-          }
-    }
     if (EXTRA && kl != nullptr && threadIdx.x < 32) {
       const int id = tb[kQryId * 32 + threadIdx.x];
       if ((unsigned)id < (unsigned)n_grows) atomicAdd(&kl[id], tf[kQryKl * 32 + threadIdx.x]);
     }
     store_step(st + 1);
   }
+  dq_idx_step(n_steps - 1);   // its dz^T was completed by the loop's last barrier
 
   // Flush the wave's dK, dV (group g) and dk_idx (shared by the groups):
   // C layout [d rows][16 keys] -> LDS [16 keys][d] -> atomics of whole key rows.
