@@ -143,10 +143,11 @@ struct BwdScratch {
   float* D;            // [B, N, H_q]   rowsum(dO * O)
   float2* idx_part;    // [B, N, H_kv, topk] per-slot (max, sum) of the index logits
   float* lse_idx;      // [B, N, H_kv]  index log-sum-exp over the selected support
-  float* dq_acc;       // [B, N, H_q, d]  fp32
+  bf16* dq_part;       // [B, chunk, topk, H_q, d] + 1 spare row: dQ partials per selected block
   float* dk_acc;       // [B, N, H_kv, d] fp32
   float* dv_acc;       // [B, N, H_kv, d] fp32
 };
+int bwd_chunk_queries(const Problem& P);
 size_t sparse_bwd_scratch_bytes(const Problem& P);
 void sparse_bwd_scratch_carve(const Problem& P, void* ws, BwdScratch* w);
 hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w,

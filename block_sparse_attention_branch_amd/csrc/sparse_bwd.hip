@@ -20,26 +20,17 @@
 //   idx_lse_kernel       per (KV block, selecting queries): log-sum-exp of
 //                        the index logits over the block (KV-outer, MFMA)
 //   idx_lse_merge_kernel lse_idx[b,t,g] over the selected support
-//   bwd_main_kernel      per work item (KV block j of group g, <= 1024 + 128
-//                        queries that selected it): 4 waves, wave w owns keys
-//                        32w..32w+31 and keeps dK, dV, dk_idx of those keys in
-//                        registers; per 32 (query, head) rows it rebuilds
-//                        S = Q K^T and P, dP = dO V^T, dS = P (dP - D), the
-//                        index logits, p_px and the head-averaged teacher
-//                        pbar, dz = lam (p_px - pbar); dS and dz go through LDS
-//                        to form dQ = dS K and dq_idx = dz K_idx (fp32
-//                        atomics); the block's dK, dV, dk_idx are added once
-//                        per item.
-//   bwd_finalize_kernel  fp32 accumulators -> bf16 dq, dk, dv.
-#include "msa_internal.h"
-
-#include <type_traits>
-
-namespace msa {
-namespace {
-
-constexpr int kItemQueries = 128;
-
+//   bwd_main16_kernel    per query chunk and work item (KV block j of group g,
+//                        its own queries and up to 1024 list entries): 8 waves
+//                        of 16 keys keep dK, dV, dk_idx in registers; per 32
+//                        (query, head) rows they rebuild S and P, dP, dS, the
+//                        index logits, p_px, the head-averaged teacher pbar and
+//                        dz = lam (p_px - pbar); dS and dz go through LDS to
+//                        form dQ = dS K (stored as a bf16 partial per selected
+//                        block) and dq_idx = dz K_idx (fp32 atomics); the
+//                        block's dK, dV, dk_idx are added once per item.
+//   dq_merge_kernel      dq = sum of a row's partials over its valid slots
+//   f32_to_bf16_kernel   fp32 accumulators -> bf16 dk, dv.
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O)
 // ---------------------------------------------------------------------------
@@ -219,7 +210,7 @@ enum : int {
   kRowCut,       // key u is visible to the row iff u <= cut (-1: none)
   kRowLse,       // LSE * log2(e)
   kRowD,         // rowsum(dO * O)
-  kRowId,        // (b N + t) H_q + h, or -1
+  kRowId,        // dQ partial row ((b CQ + t - c0) topk + slot) H_q + h, or -1
   kQryT,         // per query of the step: t or -1
   kQrySlot,      // position of block j in the query's selection
   kQryCut,       // visibility cut-off of the query (-1: none)
@@ -259,7 +250,8 @@ struct BigItem {
 
 __device__ inline bool decode_big_item(const int32_t* __restrict__ tiles, const int32_t* __restrict__ pos,
                                        const int32_t* __restrict__ offs, const int32_t* __restrict__ rows,
-                                       int n_lists, int N, int H_kv, int topk, int nblk, int nsb, BigItem* it) {
+                                       int n_lists, int N, int H_kv, int topk, int nblk, int nsb, int s_lo,
+                                       int s_hi, int jb_lo, int jb_hi, BigItem* it) {
   const int w = xcd_item(tiles[n_lists]);
   if (w < 0) return false;
   int lo = 0, hi = n_lists - 1;
@@ -272,26 +264,26 @@ __device__ inline bool decode_big_item(const int32_t* __restrict__ tiles, const 
   const int bg = lo / nblk;
   it->g = bg % H_kv;
   it->b = bg / H_kv;
-  const int len = pos[((size_t)bg * (nsb + 1) + nsb) * nblk + it->j];
-  it->n_own = li == 0 ? kBlock : 0;
-  it->e0 = li * kBigItem;
-  it->ne = max(0, min(kBigItem, len - it->e0));
+  // The list entries of the query chunk: super-blocks [s_lo, s_hi) of list j.
+  const int32_t* pb = pos + (size_t)bg * (nsb + 1) * nblk + it->j;
+  const int seg0 = pb[(size_t)s_lo * nblk], seg1 = pb[(size_t)s_hi * nblk];
+  const bool diag = it->j >= jb_lo && it->j < jb_hi;
+  it->n_own = (li == 0 && diag) ? kBlock : 0;
+  it->e0 = seg0 + li * kBigItem;
+  it->ne = max(0, min(kBigItem, seg1 - it->e0));
   it->ent = rows + (size_t)bg * N * topk + offs[(size_t)bg * (nblk + 1) + it->j];
   return true;
 }
 
-// t (-1 when qi is past the item) and, when asked, the slot of block j in the
-// query's row.
+// t (-1 when qi is past the item) and the slot of block j in the query's row.
 __device__ inline int big_query(const BigItem& it, int qi, const int32_t* __restrict__ block_idx, int N, int H_kv,
-                                int topk, bool want_slot, int* slot) {
+                                int topk, int* slot) {
   *slot = 0;
   if (qi < it.n_own) {
     const int t = it.j * kBlock + qi;
-    if (want_slot) {
-      const int32_t* brow = block_idx + (((size_t)it.b * N + t) * H_kv + it.g) * topk;
-      for (int e = 0; e < topk; ++e)
-        if (brow[e] == it.j) *slot = e;
-    }
+    const int32_t* brow = block_idx + (((size_t)it.b * N + t) * H_kv + it.g) * topk;
+    for (int e = 0; e < topk; ++e)
+      if (brow[e] == it.j) *slot = e;
     return t;
   }
   const int ei = qi - it.n_own;
@@ -391,8 +383,7 @@ template <int D, int DIDX>
 struct Bwd16Cfg {
   using TQ = Tile16Of<D>;                  // Q, dO, K, V tiles
   using TI = Pad<DIDX + 8>;                // q_idx, K_idx tiles
-  using TS = Pad<32 + 16>;                 // dS^T, dz^T: one row of 32 step rows per key; a 96-byte
-                                           // pitch keeps the transpose reads of 8 rows conflict-free
+  using TS = Pad<32 + 8>;                  // dS^T, dz^T: one row of 32 step rows per key (+16 B)
   static constexpr int PQ = TQ::pitch, PQI = TI::pitch, PST = TS::pitch;
   static constexpr size_t OFF_QS = 0;                                    // Q        [32][PQ]
   static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;        // dO       [32][PQ]
@@ -404,7 +395,10 @@ struct Bwd16Cfg {
   static constexpr size_t OFF_VS = OFF_KS + (size_t)kBlock * PQ * 2;     // V      [128][PQ]
   static constexpr size_t OFF_KIS = OFF_VS + (size_t)kBlock * PQ * 2;    // K_idx  [128][PQI]
   static constexpr size_t OFF_QL = OFF_KIS + (size_t)kBlock * PQI * 2;   // item queries: (t << 6) | slot
-  static constexpr size_t LDS = OFF_QL + (size_t)(kBlock + kBigItem) * 4;
+  static constexpr int KPQ = kW16 / (D / 16);                             // key parts of the dQ product
+  static constexpr int PDQ = D + 4;                                       // dQ tile row pitch (fp32)
+  static constexpr size_t OFF_DQ = OFF_QL + (size_t)(kBlock + kBigItem) * 4;   // dQ [KPQ][32][PDQ] fp32
+  static constexpr size_t LDS = OFF_DQ + (size_t)KPQ * 32 * PDQ * 4;
   // The flush at the end of an item reuses [OFF_KS, OFF_QL) as 8 x [16][D + 4] fp32.
   static_assert(OFF_QL - OFF_KS >= (size_t)kW16 * 16 * (D + 4) * 4, "flush scratch");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
@@ -416,11 +410,11 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dv,
     const bf16* __restrict__ q_idx, const bf16* __restrict__ k_idx, const float* __restrict__ lse_idx,
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ pos, const int32_t* __restrict__ offs,
-    const int32_t* __restrict__ rows, const int32_t* __restrict__ tiles, float* __restrict__ dq_acc,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ tiles, bf16* __restrict__ dq_part,
     float* __restrict__ dk_acc, float* __restrict__ dv_acc, float* __restrict__ dq_idx,
     float* __restrict__ dk_idx, float* __restrict__ dscore, float* __restrict__ kl, int N, int H_kv, int topk,
-    int causal, int nblk, int nsb, int n_lists, float scale, float scale_idx, float lam, int n_qrows,
-    int n_grows) {
+    int causal, int nblk, int nsb, int n_lists, float scale, float scale_idx, float lam, int n_prow,
+    int n_grows, int c0, int CQ, int s_lo, int s_hi) {
   using C = Bwd16Cfg<D, DIDX>;
   constexpr int KS = D / 32;        // 32-wide k-steps over d
   constexpr int KSI = DIDX / 32;    // 32-wide k-steps over d_idx
@@ -447,9 +441,12 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   bf16* Vs = reinterpret_cast<bf16*>(smem + C::OFF_VS);
   bf16* KIs = reinterpret_cast<bf16*>(smem + C::OFF_KIS);
   int* qlist = reinterpret_cast<int*>(smem + C::OFF_QL);   // (t << 6) | slot, or -1
+  float* dQt = reinterpret_cast<float*>(smem + C::OFF_DQ);  // a step's dQ tile, one slice per key part
 
   BigItem it;
-  if (!decode_big_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, &it)) return;
+  if (!decode_big_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, s_lo, s_hi, c0 / kBlock,
+                       (c0 + CQ + kBlock - 1) / kBlock, &it))
+    return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, lq = lane >> 4;            // C layout: column c, rows 4 lq + v
   const int H_q = H_kv * G;
@@ -458,11 +455,10 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   const int u = j * kBlock + key;
   const size_t blk_row0 = ((size_t)b * N + (size_t)j * kBlock) * H_kv + g;   // key 0 of the block
   const int nq = it.n_own + it.ne;
-  const bool want_slot = EXTRA && dscore != nullptr;
 
   for (int qi = threadIdx.x; qi < nq; qi += kT16) {
     int slot;
-    const int t = big_query(it, qi, block_idx, N, H_kv, topk, want_slot, &slot);
+    const int t = big_query(it, qi, block_idx, N, H_kv, topk, &slot);
     qlist[qi] = t < 0 ? -1 : ((t << 6) | slot);
   }
   for (int cc = threadIdx.x; cc < kBlock * CPR; cc += kT16) {
@@ -523,7 +519,9 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
       pre.t = t;
       pre.cut = cutoff(st * TQ + ld_rr / G, t);
       const size_t qrow = ((size_t)b * N + (t < 0 ? 0 : t)) * H_q + g * G + ld_rr % G;
-      pre.id = t < 0 ? -1 : (int)qrow;
+      // dQ partial row of (t, head, slot) within the query chunk.
+      const bool in_chunk = t >= c0 && t < c0 + CQ;
+      pre.id = in_chunk ? (((b * CQ + (t - c0)) * topk + (pk_e & 63)) * H_q + g * G + ld_rr % G) : -1;
       pre.q = *reinterpret_cast<const bf16x8*>(q + qrow * D + ld_col);
       pre.d = *reinterpret_cast<const bf16x8*>(dO + qrow * D + ld_col);
       pre.lse = lse[qrow];
@@ -600,6 +598,33 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
           if ((unsigned)id < (unsigned)n_grows) atomicAdd(dq_idx + (size_t)id * DIDX + 16 * ict + c, o[t][e]);
         }
   };
+  // Store step st's dQ rows from its tile in LDS as bf16 partials (one row of
+  // d values per (query, head, slot)): wave w takes rows 4w .. 4w+3, 16 bytes
+  // per lane, whole rows per instruction.  A row without a query goes to the
+  // spare row n_prow, so the stores are unconditional; every row index is
+  // checked against the partial rows before it becomes an address.
+  auto dq_store = [&](int st) {
+    constexpr int LPR = D / 8;                          // lanes per row
+    const int* tb = tabs + (st & 1) * NT;
+    const int row = 4 * wave + (lane / LPR) % 4;
+    const int col = (lane % LPR) * 8;
+    if (lane < 4 * LPR) {
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kp = 0; kp < C::KPQ; ++kp) {
+        const float4 a0 = *reinterpret_cast<const float4*>(dQt + (kp * 32 + row) * C::PDQ + col);
+        const float4 a1 = *reinterpret_cast<const float4*>(dQt + (kp * 32 + row) * C::PDQ + col + 4);
+        x[0] += a0.x; x[1] += a0.y; x[2] += a0.z; x[3] += a0.w;
+        x[4] += a1.x; x[5] += a1.y; x[6] += a1.z; x[7] += a1.w;
+      }
+      bf16x8 y;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = (bf16)x[i];
+      const int id = tb[kRowId * 32 + row];
+      const int dst = (unsigned)id < (unsigned)n_prow ? id : n_prow;
+      *reinterpret_cast<bf16x8*>(dq_part + (size_t)dst * D + col) = y;
+    }
+  };
   peek(0);
   load_step(0);
   store_step(0);
@@ -613,6 +638,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     if (st > 0) dq_idx_step(st - 1);
     load_step(st + 1);
     peek(st + 2);
+    if (st > 0) dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
 
     // S, dP (two row tiles) and the index logits (NTQ query-row tiles): lane
     // = key, slots = rows.
@@ -706,11 +732,10 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     }
     __syncthreads();   // dS^T, dz^T and the KL partials complete
 
-    // dQ[rows, column tile qct] = dS K over key part qkp: lane = column,
-    // slots = rows, one atomic instruction per (tile, slot) covering 4 rows x
-    // 16 consecutive floats.  A row without a query adds 0 at the step's first
-    // row (always a real one), so the atomics are unconditional.  Every id is
-    // checked against the row count before it becomes an address.
+    // dQ[rows, column tile qct] = dS K over key part qkp (lane = column, slots
+    // = rows) into the step's dQ tile in LDS; the tile leaves as bf16 partials
+    // at the top of the next step, whose barrier completes it.  Nothing reads
+    // the tile between the barrier above and this write.
     {
       f32x4 o[2];
 #pragma unroll
@@ -722,18 +747,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
           o[t] = mma16(tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane),
                        tr16<typename C::TQ>(Ks, 16 * qct, k0, k0 + 16, lane), o[t]);
         }
-      }
-      const int id0r = tb[kRowId * 32];
-      const int id0 = (unsigned)id0r < (unsigned)n_qrows ? id0r : 0;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int4 id4 = *reinterpret_cast<const int4*>(tb + kRowId * 32 + 16 * t + 4 * lq);
-        const int ids[4] = {id4.x, id4.y, id4.z, id4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = (unsigned)ids[e] < (unsigned)n_qrows;
-          atomicAdd(dq_acc + (size_t)(ok ? ids[e] : id0) * D + 16 * qct + c, ok ? o[t][e] : 0.f);
-        }
+        for (int e = 0; e < 4; ++e) dQt[(qkp * 32 + 16 * t + 4 * lq + e) * C::PDQ + 16 * qct + c] = o[t][e];
       }
     }
     if (EXTRA && kl != nullptr && threadIdx.x < 32) {
@@ -743,6 +758,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     store_step(st + 1);
   }
   dq_idx_step(n_steps - 1);   // its dz^T was completed by the loop's last barrier
+  __syncthreads();            // the last step's dQ tile complete
+  dq_store(n_steps - 1);
 
   // Flush the wave's dK, dV (group g) and dk_idx (shared by the groups):
   // C layout [d rows][16 keys] -> LDS [16 keys][d] -> atomics of whole key rows.
@@ -762,6 +779,63 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   flush(acc_dk, DT, D, dk_acc + kv0 * D, (size_t)H_kv * D);
   flush(acc_dv, DT, D, dv_acc + kv0 * D, (size_t)H_kv * D);
   flush(acc_dki, DTI, DIDX, dk_idx + ((size_t)b * N + (size_t)j * kBlock + 16 * wave) * DIDX, (size_t)DIDX);
+}
+
+// dq of every (query, head) of a query chunk: the sum, in fp32, of its bf16
+// partials over the valid slots of its selection (one partial per selected
+// block, written by the main kernel; layout [b, query, slot, head, d], so the
+// heads of one query and slot are contiguous on both sides).  D / 8 lanes per
+// row, 16 bytes each; the partials are read 8 slots at a time with all 8 loads
+// in flight.  Padded slots hold unwritten memory and are excluded by selection.
+template <int D>
+__global__ __launch_bounds__(256) void dq_merge_kernel(const bf16* __restrict__ part,
+                                                       const int32_t* __restrict__ block_idx, bf16* __restrict__ dq,
+                                                       int B, int N, int H_kv, int G, int topk, int c0, int CQ) {
+  constexpr int LPR = D / 8;
+  constexpr int MAXK = 32, CH = 8;
+  const int H_q = H_kv * G;
+  const size_t row = (size_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  if (row >= (size_t)B * CQ * H_q) return;
+  const int col = (threadIdx.x % LPR) * 8;
+  const int h = (int)(row % H_q);
+  const size_t bt = row / H_q;
+  const int tl = (int)(bt % CQ), b = (int)(bt / CQ);
+  const int t = c0 + tl, g = h / G;
+  const int32_t* brow = block_idx + (((size_t)b * N + t) * H_kv + g) * topk;
+  bool ok[MAXK];
+#pragma unroll
+  for (int e = 0; e < MAXK; ++e) ok[e] = false;
+  if ((topk & 3) == 0) {
+#pragma unroll
+    for (int e = 0; e < MAXK; e += 4)
+      if (e < topk) {
+        const int4 bi = *reinterpret_cast<const int4*>(brow + e);
+        ok[e] = bi.x >= 0; ok[e + 1] = bi.y >= 0; ok[e + 2] = bi.z >= 0; ok[e + 3] = bi.w >= 0;
+      }
+  } else {
+#pragma unroll
+    for (int e = 0; e < MAXK; ++e)
+      if (e < topk) ok[e] = brow[e] >= 0;
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const bf16* prow = part + (bt * topk * H_q + h) * D + col;   // slot e at + e H_q D
+#pragma unroll
+  for (int e0 = 0; e0 < MAXK; e0 += CH) {
+    if (e0 >= topk) break;
+    bf16x8 raw[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (e0 + i < topk) raw[i] = *reinterpret_cast<const bf16x8*>(prow + (size_t)(e0 + i) * H_q * D);
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (e0 + i < topk && ok[e0 + i])
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) acc[k2] += (float)raw[i][k2];
+  }
+  bf16x8 y;
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) y[k2] = (bf16)acc[k2];
+  *reinterpret_cast<bf16x8*>(dq + (((size_t)b * N + t) * H_q + h) * D + col) = y;
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst,
@@ -785,7 +859,7 @@ hipError_t to_bf16(const float* src, void* dst, size_t n, hipStream_t s) {
 
 template <int D, int DIDX, int G>
 hipError_t run_main(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w, int grid,
-                    hipStream_t s) {
+                    int c0, int CQ, int s_lo, int s_hi, hipStream_t s) {
   using C = Bwd16Cfg<D, DIDX>;
   // The optional per-score outputs get their own instantiation so that the
   // plain training path carries none of their registers.
@@ -797,33 +871,49 @@ hipError_t run_main(const Problem& P, const BwdArgs& a, const BlockMap& m, const
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kT16), C::LDS, s, static_cast<const bf16*>(a.q),
                      static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dO),
                      a.lse, w.D, static_cast<const bf16*>(a.q_idx), static_cast<const bf16*>(a.k_idx), w.lse_idx,
-                     a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.dq_acc, w.dk_acc, w.dv_acc, a.dq_idx,
+                     a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.dq_part, w.dk_acc, w.dv_acc, a.dq_idx,
                      a.dk_idx, a.dscore, a.kl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb,
-                     P.B * P.H_kv * P.nblk, P.scale, P.scale_idx, a.kl_weight, P.B * P.N * P.H_q,
-                     P.B * P.N * P.H_kv);
+                     P.B * P.H_kv * P.nblk, P.scale, P.scale_idx, a.kl_weight, P.B * CQ * P.H_q * P.topk,
+                     P.B * P.N * P.H_kv, c0, CQ, s_lo, s_hi);
   return hipGetLastError();
 }
 
 template <int D, int DIDX>
-hipError_t run_main_g(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w, int grid,
-                      hipStream_t s) {
+hipError_t run_main_g(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w, int grid, int c0,
+                      int CQ, int s_lo, int s_hi, hipStream_t s) {
   switch (P.G) {
-    case 1: return run_main<D, DIDX, 1>(P, a, m, w, grid, s);
-    case 2: return run_main<D, DIDX, 2>(P, a, m, w, grid, s);
-    case 4: return run_main<D, DIDX, 4>(P, a, m, w, grid, s);
-    case 8: return run_main<D, DIDX, 8>(P, a, m, w, grid, s);
-    case 16: return run_main<D, DIDX, 16>(P, a, m, w, grid, s);
+    case 1: return run_main<D, DIDX, 1>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
+    case 2: return run_main<D, DIDX, 2>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
+    case 4: return run_main<D, DIDX, 4>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
+    case 8: return run_main<D, DIDX, 8>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
+    case 16: return run_main<D, DIDX, 16>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+int bwd_chunk_queries(const Problem& P) {
+  // Queries per chunk of the main kernel: their dQ partials (bf16, one row per
+  // (query, slot, head)) must fit in 40 GiB (one chunk at N = 128K with 64
+  // heads); a multiple of the block map's super-block span, since chunks select
+  // list entries by super-block.
+  const size_t per_query = (size_t)P.B * P.H_q * P.topk * P.d * 2;
+  const size_t cap = size_t(40) << 30;
+  const size_t span = (size_t)block_map_super_span(P);
+  size_t q = cap / per_query;
+  q -= q % span;
+  if (q < span) q = span;
+  if (q >= (size_t)P.N) q = P.N;
+  return (int)q;
+}
+
 size_t sparse_bwd_scratch_bytes(const Problem& P) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t rows_q = (size_t)P.B * P.N * P.H_q;
   const size_t rows_g = (size_t)P.B * P.N * P.H_kv;
-  return al(rows_q * 4) + al(rows_g * P.topk * 8) + al(rows_g * 4) + al(rows_q * P.d * 4) +
+  const size_t part_rows = (size_t)P.B * bwd_chunk_queries(P) * P.H_q * P.topk + 1;   // + the spare row
+  return al(rows_q * 4) + al(rows_g * P.topk * 8) + al(rows_g * 4) + al(part_rows * P.d * 2) +
          2 * al(rows_g * P.d * 4);
 }
 
@@ -831,6 +921,7 @@ void sparse_bwd_scratch_carve(const Problem& P, void* ws, BwdScratch* w) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t rows_q = (size_t)P.B * P.N * P.H_q;
   const size_t rows_g = (size_t)P.B * P.N * P.H_kv;
+  const size_t part_rows = (size_t)P.B * bwd_chunk_queries(P) * P.H_q * P.topk + 1;
   char* p = static_cast<char*>(ws);
   w->D = reinterpret_cast<float*>(p);
   p += al(rows_q * 4);
@@ -838,8 +929,8 @@ void sparse_bwd_scratch_carve(const Problem& P, void* ws, BwdScratch* w) {
   p += al(rows_g * P.topk * 8);
   w->lse_idx = reinterpret_cast<float*>(p);
   p += al(rows_g * 4);
-  w->dq_acc = reinterpret_cast<float*>(p);
-  p += al(rows_q * P.d * 4);
+  w->dq_part = reinterpret_cast<bf16*>(p);
+  p += al(part_rows * P.d * 2);
   w->dk_acc = reinterpret_cast<float*>(p);
   p += al(rows_g * P.d * 4);
   w->dv_acc = reinterpret_cast<float*>(p);
@@ -852,7 +943,6 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
   const size_t rows_g = (size_t)P.B * P.N * P.H_kv;
   // Zero every accumulator (fill kernels: safe inside captured graphs).
   prof_begin("bwd_prep", s);
-  if ((e = launch_fill_f32(w.dq_acc, rows_q * P.d, 0.f, s)) != hipSuccess) return e;
   if ((e = launch_fill_f32(w.dk_acc, rows_g * P.d, 0.f, s)) != hipSuccess) return e;
   if ((e = launch_fill_f32(w.dv_acc, rows_g * P.d, 0.f, s)) != hipSuccess) return e;
   if ((e = launch_fill_f32(a.dq_idx, rows_g * P.d_idx, 0.f, s)) != hipSuccess) return e;
@@ -891,22 +981,41 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
                      a.block_idx, w.lse_idx, rows_g, P.topk);
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // Long items (own queries + up to kBigItem list entries) for the main kernel.
-  if ((e = launch_block_items(P, m, 0, P.N, kBigItem, s, 1)) != hipSuccess) return e;
-  grid = block_items_upper_bound(P, 0, P.N, kBigItem);
-  grid = (grid + 7) & ~size_t(7);
-  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  // Fused main + index backward.
-  prof_begin("bwd_main", s);
-  if (P.d == 128 && P.d_idx == 64) e = run_main_g<128, 64>(P, a, m, w, (int)grid, s);
-  else if (P.d == 128) e = run_main_g<128, 32>(P, a, m, w, (int)grid, s);
-  else if (P.d_idx == 64) e = run_main_g<64, 64>(P, a, m, w, (int)grid, s);
-  else e = run_main_g<64, 32>(P, a, m, w, (int)grid, s);
-  prof_end(s);
-  if (e != hipSuccess) return e;
+  // Main kernel per query chunk (long items: own queries + up to kBigItem
+  // list entries), then the chunk's dq from its partials.
+  const int chunk = bwd_chunk_queries(P);
+  const int span = block_map_super_span(P);
+  for (int c0 = 0; c0 < P.N; c0 += chunk) {
+    const int c1 = c0 + chunk < P.N ? c0 + chunk : P.N;
+    const int CQ = c1 - c0;
+    if ((e = launch_block_items(P, m, c0, c1, kBigItem, s, 1)) != hipSuccess) return e;
+    size_t g2 = block_items_upper_bound(P, c0, c1, kBigItem);
+    g2 = (g2 + 7) & ~size_t(7);
+    if (g2 > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int s_lo = c0 / span;
+    const int s_hi = (c1 == P.N) ? m.nsb : c1 / span;
+    prof_begin("bwd_main", s);
+    if (P.d == 128 && P.d_idx == 64) e = run_main_g<128, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+    else if (P.d == 128) e = run_main_g<128, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+    else if (P.d_idx == 64) e = run_main_g<64, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+    else e = run_main_g<64, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+    prof_end(s);
+    if (e != hipSuccess) return e;
+    const size_t rows = (size_t)P.B * CQ * P.H_q;
+    const int rpb = 256 / (P.d / 8);
+    const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
+    prof_begin("bwd_dq_merge", s);
+    if (P.d == 128)
+      hipLaunchKernelGGL(dq_merge_kernel<128>, dim3(blocks), dim3(256), 0, s, w.dq_part, a.block_idx,
+                         static_cast<bf16*>(a.dq), P.B, P.N, P.H_kv, P.G, P.topk, c0, CQ);
+    else
+      hipLaunchKernelGGL(dq_merge_kernel<64>, dim3(blocks), dim3(256), 0, s, w.dq_part, a.block_idx,
+                         static_cast<bf16*>(a.dq), P.B, P.N, P.H_kv, P.G, P.topk, c0, CQ);
+    prof_end(s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // fp32 accumulators to bf16 outputs.
   prof_begin("bwd_finalize", s);
-  if ((e = to_bf16(w.dq_acc, a.dq, rows_q * P.d, s)) != hipSuccess) return e;
   if ((e = to_bf16(w.dk_acc, a.dk, rows_g * P.d, s)) != hipSuccess) return e;
   e = to_bf16(w.dv_acc, a.dv, rows_g * P.d, s);
   prof_end(s);

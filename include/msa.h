@@ -167,8 +167,10 @@ MSA_API int msa_sparse_fwd(const msa_dims* dims, const void* q, const void* k, c
  *          block_idx[slot]*block_size + offset, 0 where masked or padded.
  *          Meant for tests (it is large).
  *   kl     out nullable [B,N,H_kv] fp32: KL(pbar || p_px) per row, unweighted.
- * Only dtype bf16 is supported here.  Gradients accumulate in fp32 with
- * atomics, so their last bits may vary from run to run.
+ * Only dtype bf16 is supported here.  dq is deterministic: each selected
+ * block's contribution is stored as a bf16 partial and the partials of a row
+ * are summed in fp32 in a fixed order.  dk, dv, dq_idx, dk_idx (and kl)
+ * accumulate in fp32 with atomics, so their last bits may vary from run to run.
  */
 MSA_API size_t msa_sparse_bwd_workspace(const msa_dims* dims);
 MSA_API int msa_sparse_bwd(const msa_dims* dims, const void* q, const void* k, const void* v,
