@@ -31,6 +31,15 @@
 //                        block's dK, dV, dk_idx are added once per item.
 //   dq_merge_kernel      dq = sum of a row's partials over its valid slots
 //   f32_to_bf16_kernel   fp32 accumulators -> bf16 dk, dv.
+#include "msa_internal.h"
+
+#include <type_traits>
+
+namespace msa {
+namespace {
+
+constexpr int kItemQueries = 128;
+
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O)
 // ---------------------------------------------------------------------------
