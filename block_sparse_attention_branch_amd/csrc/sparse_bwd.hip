@@ -482,6 +482,10 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
   }
   const int qct = wave % DT, qkp = wave / DT;         // dQ column tile and key part
+  // The B operands of S and dP (this lane's key row of K and of V), constant
+  // over the item: held in registers, which takes a third of the step's LDS
+  // operand traffic off the S / dP products.
+  bf16x8 kfr[KS], vfr[KS];
   const int ict = wave % DTI, ikp = wave / DTI;       // dq_idx column tile and key part
 
   f32x4 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
@@ -493,6 +497,11 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 #pragma unroll
   for (int i = 0; i < DTI; ++i) acc_dki[i] = zero4();
   __syncthreads();   // item query list and the K, V, K_idx tiles ready
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kfr[ks] = *reinterpret_cast<const bf16x8*>(Ks + C::TQ::off(key, 32 * ks + 8 * lq));
+    vfr[ks] = *reinterpret_cast<const bf16x8*>(Vs + C::TQ::off(key, 32 * ks + 8 * lq));
+  }
 
   // Per-thread share of a step, loaded one step ahead: one 16-byte chunk of
   // Q and of dO (thread < 32 CPR) with the row's statistics when the chunk is
@@ -659,10 +668,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int col = 32 * ks + 8 * lq;
-        s[t] = mma16(*reinterpret_cast<const bf16x8*>(Qs + C::TQ::off(16 * t + c, col)),
-                     *reinterpret_cast<const bf16x8*>(Ks + C::TQ::off(key, col)), s[t]);
-        dp[t] = mma16(*reinterpret_cast<const bf16x8*>(dOs + C::TQ::off(16 * t + c, col)),
-                      *reinterpret_cast<const bf16x8*>(Vs + C::TQ::off(key, col)), dp[t]);
+        s[t] = mma16(*reinterpret_cast<const bf16x8*>(Qs + C::TQ::off(16 * t + c, col)), kfr[ks], s[t]);
+        dp[t] = mma16(*reinterpret_cast<const bf16x8*>(dOs + C::TQ::off(16 * t + c, col)), vfr[ks], dp[t]);
       }
     }
 #pragma unroll
