@@ -118,6 +118,24 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
   store_block(0);
   __syncthreads();
 
+  // Insert a block's pooled score into the lane's sorted list (strictly
+  // greater wins, so equal scores keep the lower block index).
+  auto insert = [&](float p, int jb) {
+#pragma unroll
+    for (int i = CAP - 1; i >= 1; --i) {
+      const bool up = p > tv[i - 1];
+      const bool here = p > tv[i];
+      tv[i] = up ? tv[i - 1] : (here ? p : tv[i]);
+      ti[i] = up ? ti[i - 1] : (here ? jb : ti[i]);
+    }
+    const bool here = p > tv[0];
+    tv[0] = here ? p : tv[0];
+    ti[0] = here ? jb : ti[0];
+  };
+  // The insertion of block j-1 runs after block j's products are issued, so
+  // its arithmetic overlaps the matrix unit instead of following it.
+  float p_prev = -INFINITY;
+  int j_prev = -1;
   for (int j = 0; j <= jlast; ++j) {
     const int buf = j & 1;
     const bool more = j < jlast;
@@ -127,30 +145,39 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
     if (visible && (!is_own || pooled != nullptr)) {
       float run0 = -INFINITY, run1 = -INFINITY;
       const T* tile = lds + buf * C::TILE_ELEMS;
+      f32x16 a0[4], a1[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x16 a0 = zero16(), a1 = zero16();
+        a0[mt] = zero16();
+        a1[mt] = zero16();
         const T* ap = tile + (mt * 32 + (lane & 31)) * C::PITCH + KPL * (lane >> 5);
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
           const typename M::frag a = M::load(ap + ks * 2 * KPL);
-          a0 = M::mma(a, qf[0][ks], a0);
-          a1 = M::mma(a, qf[1][ks], a1);
+          a0[mt] = M::mma(a, qf[0][ks], a0[mt]);
+          a1[mt] = M::mma(a, qf[1][ks], a1[mt]);
         }
+      }
+      if (j_prev >= 0) {
+        insert(p_prev, j_prev);
+        j_prev = -1;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
         if (is_own && causal) {
           // Diagonal block: only keys u <= t are visible to query t.
           const int t0 = q0 + (lane & 31);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int u = j * kBlock + mt * 32 + c_row(v, lane);
-            if (u > t0) a0[v] = -INFINITY;
-            if (u > t0 + 32) a1[v] = -INFINITY;
+            if (u > t0) a0[mt][v] = -INFINITY;
+            if (u > t0 + 32) a1[mt][v] = -INFINITY;
           }
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          run0 = fmaxf(run0, a0[v]);
-          run1 = fmaxf(run1, a1[v]);
+          run0 = fmaxf(run0, a0[mt][v]);
+          run1 = fmaxf(run1, a1[mt][v]);
         }
       }
       // Lanes l and l^32 hold the two key halves of the same query column.
@@ -159,21 +186,14 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
       const int tq = q0 + lane;
       if (pooled != nullptr && tq < N) pooled[(((size_t)b * N + tq) * H_kv + g) * nblk + j] = p;
       if (!is_own) {
-#pragma unroll
-        for (int i = CAP - 1; i >= 1; --i) {
-          const bool up = p > tv[i - 1];
-          const bool here = p > tv[i];
-          tv[i] = up ? tv[i - 1] : (here ? p : tv[i]);
-          ti[i] = up ? ti[i - 1] : (here ? j : ti[i]);
-        }
-        const bool here = p > tv[0];
-        tv[0] = here ? p : tv[0];
-        ti[0] = here ? j : ti[0];
+        p_prev = p;
+        j_prev = j;
       }
     }
     if (more) store_block(buf ^ 1);
     __syncthreads();
   }
+  if (j_prev >= 0) insert(p_prev, j_prev);
 
   const int tq = q0 + lane;
   if (!wave_valid || tq >= N) return;
