@@ -98,11 +98,12 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Queries per forward launch: bounds the partial-result buffer (one output
 // row in the dtype plus one fp32 log-sum-exp per (batch, query, head, slot))
-// to ~8 GiB.  A multiple of the block map's super-block span.
+// to ~40 GiB: one launch at N = 128K with 64 heads, four at N = 1M.  A
+// multiple of the block map's super-block span.
 int fwd_chunk_queries(const msa::Problem& P) {
   const size_t esz = P.dtype == MSA_BF16 ? 2 : 4;
   const size_t per_query = (size_t)P.B * P.H_q * P.topk * (P.d * esz + sizeof(float));
-  const size_t cap = size_t(8) << 30;
+  const size_t cap = size_t(40) << 30;   // one chunk at N = 128K with 64 heads
   const size_t span = (size_t)msa::block_map_super_span(P);
   size_t q = cap / per_query;
   q -= q % span;

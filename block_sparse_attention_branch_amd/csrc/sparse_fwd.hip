@@ -261,8 +261,11 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
     // 4 x 4 values, then lane l stores 16 bytes of row l / RPL (+ 32 / SPL..)
     // so that each store instruction writes whole 64-byte row segments.
     const float inv = 1.f / lsum;
-    const int prow = valid ? (((b * CQ + (t - c0)) * H_q + h) * topk + slot) : -1;
-    if (valid && lane < 32) plse[prow] = m * scale + logf(lsum);
+    // LSE partials [b, query, head, slot]; output partials [b, query, slot,
+    // head, d], so that the heads of one query and slot are contiguous.
+    const int lrow = valid ? (((b * CQ + (t - c0)) * H_q + h) * topk + slot) : -1;
+    const int prow = valid ? (((b * CQ + (t - c0)) * topk + slot) * H_q + h) : -1;
+    if (valid && lane < 32) plse[lrow] = m * scale + logf(lsum);
     {
       constexpr int EPC = C::EPC;                 // elements per 16-byte piece
       constexpr int PPR = 32 / EPC;               // pieces per 32-column row slice
@@ -345,14 +348,14 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po
   float acc[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-  const T* prow = po + row * topk * D + part * EPL;
+  const T* prow = po + (bt * topk * H_q + h) * D + part * EPL;   // slot e at + e H_q D
 #pragma unroll
   for (int e0 = 0; e0 < MAXK; e0 += CH) {
     if (e0 >= topk) break;
     uint4 raw[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i)
-      if (e0 + i < topk) raw[i] = *reinterpret_cast<const uint4*>(prow + (size_t)(e0 + i) * D);
+      if (e0 + i < topk) raw[i] = *reinterpret_cast<const uint4*>(prow + (size_t)(e0 + i) * H_q * D);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int e = e0 + i;

@@ -92,16 +92,29 @@ def sample_rows(B, N, n, seed, extra=()):
     return sorted(set(rows))
 
 
-def fwd_chunk_queries(w: msa_inputs.Workload) -> int:
-    """Queries per forward launch, as the library plans it (for sampling rows
-    at chunk seams)."""
-    esz = 2 if w.dtype == "bf16" else 4
-    per_q = w.B * w.H_q * w.topk * (w.d * esz + 4)
+def _super_span(w: msa_inputs.Workload) -> int:
     nblk = w.N // w.block_size
     sb = 1
     while sb < 64 and ((nblk + sb - 1) // sb + 1) * nblk * 4 * w.B * w.H_kv > (256 << 20):
         sb *= 2
-    span = sb * w.block_size
-    q = (8 << 30) // per_q
+    return sb * w.block_size
+
+
+def _chunk(w: msa_inputs.Workload, per_q: int) -> int:
+    span = _super_span(w)
+    q = (40 << 30) // per_q
     q -= q % span
     return max(span, min(q, w.N))
+
+
+def fwd_chunk_queries(w: msa_inputs.Workload) -> int:
+    """Queries per forward launch, as the library plans it (for sampling rows
+    at chunk seams): partials of at most 40 GiB."""
+    esz = 2 if w.dtype == "bf16" else 4
+    return _chunk(w, w.B * w.H_q * w.topk * (w.d * esz + 4))
+
+
+def bwd_chunk_queries(w: msa_inputs.Workload) -> int:
+    """Queries per backward main-kernel launch (bf16 dQ partials of at most
+    40 GiB), for sampling rows at its chunk seams."""
+    return _chunk(w, w.B * w.H_q * w.topk * w.d * 2)

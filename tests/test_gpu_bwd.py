@@ -12,7 +12,7 @@ import torch
 
 import msa_inputs
 from oracle import msa_oracle as O
-from tests.gpu_helpers import cosine, f32, max_rel, need_gpu, sample_rows, say
+from tests.gpu_helpers import bwd_chunk_queries, cosine, f32, max_rel, need_gpu, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,10 @@ def _sampled(w, variant, n_rows, seed, blocks):
     and dk_idx of sampled KV blocks of batch 0, recomputed from every row that
     selected them."""
     x, sel, gr = _run(w, variant, want_kl=True)
-    rows = sample_rows(w.B, w.N, n_rows, seed)
+    chunk = bwd_chunk_queries(w)
+    seams = [c + dt for c in range(chunk, w.N, chunk) for dt in (-1, 0, 1)]
+    rows = sample_rows(w.B, w.N, n_rows, seed, extra=seams)
+    say(f"  main-kernel chunk {chunk} queries, {len(seams)} seam rows")
     bt = torch.tensor(rows, dtype=torch.long)
     s = sel.cpu().numpy().astype(np.int64)
     k_h, v_h, ki_h = f32(x["k"]), f32(x["v"]), f32(x["k_idx"])
