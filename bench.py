@@ -75,7 +75,7 @@ KERNEL_SYMBOL = {
     "index_topk": "index_topk_kernel",
     "fwd_partial": "sparse_fwd_kernel",
     "fwd_merge": "fwd_merge_kernel",
-    "bwd_main": "bwd_main_kernel",
+    "bwd_main": "bwd_main16_kernel",
     "bwd_idx_lse": "idx_lse_kernel",
 }
 # The calibration copy: torch.neg over fp32, one read and one write of the buffer.
