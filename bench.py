@@ -42,6 +42,7 @@ KERNEL_SOURCE = {
     "bwd_idx_lse": "sparse_bwd.hip",
     "bwd_prep": "sparse_bwd.hip",
     "bwd_finalize": "sparse_bwd.hip",
+    "bwd_dq_merge": "sparse_bwd.hip",
     "block_map": "block_map.hip",
     "block_items": "block_map.hip",
 }
@@ -54,18 +55,26 @@ def support_pairs(N: int, block: int, topk: int) -> int:
     return int((np.minimum(topk - 1, t // block) * block + t % block + 1).sum())
 
 
+def valid_slots(N: int, block: int, topk: int) -> int:
+    """Sum over queries t of the selected blocks that exist (causal): min(k, t // block + 1)."""
+    t = np.arange(N, dtype=np.int64)
+    return int(np.minimum(topk, t // block + 1).sum())
+
+
 def algorithmic_work(w) -> dict:
     """Algorithmic work of one launch of each kernel (flops or bytes)."""
     pairs = support_pairs(w.N, w.block_size, w.topk) * w.B          # (t, u) pairs per group/head
     esz = 2 if w.dtype == "bf16" else 4
     vis = w.B * w.N * (w.N + 1) // 2                                # causally visible (t, u)
+    slots = valid_slots(w.N, w.block_size, w.topk) * w.B            # (t, selected block) per group/head
     out = {
         "index_topk": ("flop", 2.0 * w.d_idx * vis * w.H_kv),
         "fwd_partial": ("flop", 4.0 * w.d * pairs * w.H_q),
         "bwd_main": ("flop", (10.0 * w.d * w.H_q + 6.0 * w.d_idx * w.H_kv) * pairs),
         "bwd_idx_lse": ("flop", 2.0 * w.d_idx * pairs * w.H_kv),
-        # merge: read topk partials (row + fp32 lse) per (t, h), write o and lse
-        "fwd_merge": ("byte", float(w.B * w.N * w.H_q * (w.topk * (w.d * esz + 4) + w.d * esz + 4))),
+        # merges: read a (t, h)'s partials of its valid slots, write its row
+        "fwd_merge": ("byte", float(w.H_q * (slots * (w.d * esz + 4) + w.B * w.N * (w.d * esz + 4)))),
+        "bwd_dq_merge": ("byte", float(w.H_q * (slots * w.d * 2 + w.B * w.N * w.d * esz))),
     }
     return out
 
@@ -280,7 +289,8 @@ def main() -> int:
 
     sparse_flop = work["fwd_partial"][1] + (work["bwd_main"][1] if w.backward else 0.0)
     sparse_ms = sum(prof.get(n, (0, 0.0))[1] for n in ("block_map", "block_items", "fwd_partial", "fwd_merge",
-                                                        "bwd_prep", "bwd_idx_lse", "bwd_main", "bwd_finalize"))
+                                                        "bwd_prep", "bwd_idx_lse", "bwd_main", "bwd_dq_merge",
+                                                        "bwd_finalize"))
     sparse_ms /= args.steps
     sparse_tflops = sparse_flop / (sparse_ms * 1e-3) / 1e12 if sparse_ms > 0 else None
 

@@ -236,10 +236,8 @@ struct Pad {
   __device__ static int off(int r, int c) { return r * P + c; }
 };
 // Swz128b: rows of 128 elements (256 B, no padding) whose 16-byte chunk c of
-// row r is stored at chunk c ^ (2 (r & 7) + ((r >> 3) & 1)).  For the 16x16x32
-// operands: a read of one chunk from 16 consecutive rows and a
-// transpose read (32 lanes: 8 consecutive rows x 2 chunks) both hit distinct
-// chunks.
+// row r is stored at chunk c ^ (2 (r & 7) + ((r >> 3) & 1)): transpose reads
+// of 8 consecutive rows x 2 chunks hit distinct banks.  For the K and V tiles.
 struct Swz128b {
   static constexpr int pitch = 128;
   __device__ static int off(int r, int c) {   // c: a multiple of 4
@@ -247,7 +245,7 @@ struct Swz128b {
   }
 };
 template <int W>
-using Tile16Of = typename std::conditional<W == 128, Swz128b, Pad<W + 8>>::type;
+using TileKOf = typename std::conditional<W == 128, Swz128b, Pad<W + 8>>::type;
 
 // A work item of the main kernel and the queries it covers: item-local query
 // qi < n_own is t = 128 j + qi (diagonal, causal mask); otherwise it is list
@@ -388,21 +386,31 @@ __device__ inline void head_mean16(const f32x4* p, f32x4* pb) {
   }
 }
 
+// LDS tiles of the main kernel.  The gfx950 LDS serves the reads of 32 lanes
+// together, from 128 four-byte banks for 16-byte reads and from 64 banks for
+// 8-byte and transpose reads; writes use 32 banks.  Under that rule the padded
+// pitches below leave the kernel's per-step accesses free of bank conflicts:
+// the 16-byte A-operand reads of one chunk from 16 consecutive rows of Q, dO
+// and q_idx, the transpose reads of Q, dO and q_idx, and the 8-byte dS^T / dz^T
+// writes (whose transpose reads keep a 2-way conflict in one of four passes).
+// Padding folds into instruction offsets, where an XOR swizzle would hold one
+// address register per access.
 template <int D, int DIDX>
 struct Bwd16Cfg {
-  using TQ = Tile16Of<D>;                  // Q, dO, K, V tiles
-  using TI = Pad<DIDX + 8>;                // q_idx, K_idx tiles
-  using TS = Pad<32 + 8>;                  // dS^T, dz^T: one row of 32 step rows per key (+16 B)
-  static constexpr int PQ = TQ::pitch, PQI = TI::pitch, PST = TS::pitch;
+  using TQ = Pad<D + 16>;                  // Q, dO tiles (step rows)
+  using TK = TileKOf<D>;                   // K, V tiles (the block's keys)
+  using TI = Pad<DIDX + 16>;               // q_idx, K_idx tiles
+  using TS = Pad<32 + 4>;                  // dS^T, dz^T: one row of 32 step rows per key (+8 B)
+  static constexpr int PQ = TQ::pitch, PK = TK::pitch, PQI = TI::pitch, PST = TS::pitch;
   static constexpr size_t OFF_QS = 0;                                    // Q        [32][PQ]
   static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;        // dO       [32][PQ]
   static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;       // q_idx    [32][PQI]
   static constexpr size_t OFF_DST = OFF_QIS + (size_t)32 * PQI * 2;      // dS^T     [128][PST]
   static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     2 x [128][PST]
   static constexpr size_t OFF_TAB = OFF_DZT + (size_t)2 * kBlock * PST * 2;   // 2 x kNumTabs x [32]
-  static constexpr size_t OFF_KS = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K  [128][PQ]
-  static constexpr size_t OFF_VS = OFF_KS + (size_t)kBlock * PQ * 2;     // V      [128][PQ]
-  static constexpr size_t OFF_KIS = OFF_VS + (size_t)kBlock * PQ * 2;    // K_idx  [128][PQI]
+  static constexpr size_t OFF_KS = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K  [128][PK]
+  static constexpr size_t OFF_VS = OFF_KS + (size_t)kBlock * PK * 2;     // V      [128][PK]
+  static constexpr size_t OFF_KIS = OFF_VS + (size_t)kBlock * PK * 2;    // K_idx  [128][PQI]
   static constexpr size_t OFF_QL = OFF_KIS + (size_t)kBlock * PQI * 2;   // item queries: (t << 6) | slot
   static constexpr int KPQ = kW16 / (D / 16);                             // key parts of the dQ product
   static constexpr int PDQ = D + 4;                                       // dQ tile row pitch (fp32)
@@ -411,6 +419,7 @@ struct Bwd16Cfg {
   // The flush at the end of an item reuses [OFF_KS, OFF_QL) as 8 x [16][D + 4] fp32.
   static_assert(OFF_QL - OFF_KS >= (size_t)kW16 * 16 * (D + 4) * 4, "flush scratch");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
+  static_assert(PQ % 8 == 0 && PQI % 8 == 0 && PST % 4 == 0, "16-byte rows for 16-byte accesses, 8-byte for dS^T");
 };
 
 template <int D, int DIDX, int G, bool EXTRA>
@@ -473,8 +482,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   for (int cc = threadIdx.x; cc < kBlock * CPR; cc += kT16) {
     const int kk = cc / CPR, col = (cc % CPR) * 8;
     const size_t row = blk_row0 + (size_t)kk * H_kv;
-    *reinterpret_cast<bf16x8*>(Ks + C::TQ::off(kk, col)) = *reinterpret_cast<const bf16x8*>(k + row * D + col);
-    *reinterpret_cast<bf16x8*>(Vs + C::TQ::off(kk, col)) = *reinterpret_cast<const bf16x8*>(v + row * D + col);
+    *reinterpret_cast<bf16x8*>(Ks + C::TK::off(kk, col)) = *reinterpret_cast<const bf16x8*>(k + row * D + col);
+    *reinterpret_cast<bf16x8*>(Vs + C::TK::off(kk, col)) = *reinterpret_cast<const bf16x8*>(v + row * D + col);
   }
   for (int cc = threadIdx.x; cc < kBlock * CPRI; cc += kT16) {
     const int kk = cc / CPRI, col = (cc % CPRI) * 8;
@@ -499,8 +508,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   __syncthreads();   // item query list and the K, V, K_idx tiles ready
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    kfr[ks] = *reinterpret_cast<const bf16x8*>(Ks + C::TQ::off(key, 32 * ks + 8 * lq));
-    vfr[ks] = *reinterpret_cast<const bf16x8*>(Vs + C::TQ::off(key, 32 * ks + 8 * lq));
+    kfr[ks] = *reinterpret_cast<const bf16x8*>(Ks + C::TK::off(key, 32 * ks + 8 * lq));
+    vfr[ks] = *reinterpret_cast<const bf16x8*>(Vs + C::TK::off(key, 32 * ks + 8 * lq));
   }
 
   // Per-thread share of a step, loaded one step ahead: one 16-byte chunk of
@@ -761,7 +770,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         for (int ks = 0; ks < 4 / KPQ; ++ks) {
           const int k0 = 32 * (qkp * (4 / KPQ) + ks) + 4 * lq;   // keys k0 .. k0+3, k0+16 .. k0+19
           o[t] = mma16(tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane),
-                       tr16<typename C::TQ>(Ks, 16 * qct, k0, k0 + 16, lane), o[t]);
+                       tr16<typename C::TK>(Ks, 16 * qct, k0, k0 + 16, lane), o[t]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) dQt[(qkp * 32 + 16 * t + 4 * lq + e) * C::PDQ + 16 * qct + c] = o[t][e];

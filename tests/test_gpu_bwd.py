@@ -137,3 +137,25 @@ def test_bwd_128k_planted_sampled():
 def test_bwd_1m_sampled():
     w = msa_inputs.WORKLOADS["fwdbwd-bf16-n1m"]
     _sampled(w, "normal", 16, 5, blocks=[w.nblk - 1])
+
+
+def test_bwd_dq_and_forward_deterministic():
+    """dq is summed from per-block partials in a fixed order, and the forward
+    merges its partials in slot order: both are bit-identical across calls
+    (dk, dv and the index gradients use fp32 atomics and are not)."""
+    msa = need_gpu()
+    w = msa_inputs.WORKLOADS["fwdbwd-bf16-b4-n8k"]
+    say(f"[determinism] {w.name}")
+    x = msa_inputs.make_inputs(w, "normal", device="cuda", with_grad_out=True)
+    sel = msa.index_topk(x["q_idx"], x["k_idx"], topk=w.topk)
+    runs = []
+    for _ in range(2):
+        o, lse = msa.sparse_fwd(x["q"], x["k"], x["v"], sel, d_idx=w.d_idx)
+        gr = msa.sparse_bwd(x["q"], x["k"], x["v"], o, x["dO"], lse, sel, x["q_idx"], x["k_idx"])
+        runs.append((o, lse, gr["dq"]))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("o", "lse", "dq"), runs[0], runs[1]):
+        same = torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+        say(f"  {name} bit-identical: {same}")
+        assert same, name
