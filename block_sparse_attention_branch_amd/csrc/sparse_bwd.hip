@@ -303,6 +303,7 @@ __device__ inline int big_query(const BigItem& it, int qi, const int32_t* __rest
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 __device__ inline bf16x4 pack4(float a, float b, float c, float d) {
   bf16x4 r;
@@ -697,14 +698,16 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     for (int t = 0; t < 2; ++t) {
       const int r4 = 16 * t + 4 * lq;
       const int4 cut = *reinterpret_cast<const int4*>(tb + kRowCut * 32 + r4);
-      const float4 l2 = *reinterpret_cast<const float4*>(tf + kRowLse * 32 + r4);
+      // Volatile: read whole and up front, never sunk into the masked use.
+      const f32x4 l2 = *(const volatile lds_f32x4*)(tf + kRowLse * 32 + r4);
       const float4 dd = *reinterpret_cast<const float4*>(tf + kRowD * 32 + r4);
       const int cuts[4] = {cut.x, cut.y, cut.z, cut.w};
-      const float l2s[4] = {l2.x, l2.y, l2.z, l2.w};
+      const float l2s[4] = {l2[0], l2[1], l2[2], l2[3]};
       const float dds[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pv = u <= cuts[e] ? __builtin_amdgcn_exp2f(s[t][e] * c_s - l2s[e]) : 0.f;
+        // Masked by the exponent (exp2(-inf) = 0), so no branch is formed.
+        const float pv = __builtin_amdgcn_exp2f(u <= cuts[e] ? s[t][e] * c_s - l2s[e] : -INFINITY);
         p[t][e] = pv;
         ds[t][e] = pv * (dp[t][e] - dds[e]) * scale;
       }
@@ -717,14 +720,15 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     for (int t = 0; t < NTQ; ++t) {
       const int r4 = 16 * t + 4 * lq;
       const int4 qc = *reinterpret_cast<const int4*>(tb + kQryCut * 32 + r4);
-      const float4 ql = *reinterpret_cast<const float4*>(tf + kQryLse * 32 + r4);
+      const f32x4 ql = *(const volatile lds_f32x4*)(tf + kQryLse * 32 + r4);
       const int qcs[4] = {qc.x, qc.y, qc.z, qc.w};
-      const float qls[4] = {ql.x, ql.y, ql.z, ql.w};
+      const float qls[4] = {ql[0], ql[1], ql[2], ql[3]};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lz = ri[t][e] * c_i - qls[e];     // log2 p_px
         const bool vis = u <= qcs[e];                  // -1 for rows that hold no query
-        dz[t][e] = vis ? lam * (__builtin_amdgcn_exp2f(lz) - pb[t][e]) : 0.f;
+        const float ez = __builtin_amdgcn_exp2f(vis ? lz : -INFINITY);
+        dz[t][e] = vis ? lam * (ez - pb[t][e]) : 0.f;
         if (EXTRA && dscore != nullptr && vis) {
           const int tq = tb[kQryT * 32 + r4 + e], sl = tb[kQrySlot * 32 + r4 + e];
           if ((unsigned)tq < (unsigned)N && (unsigned)sl < (unsigned)topk)
