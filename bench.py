@@ -187,6 +187,114 @@ def cpu_baseline(w, x, rows_n: int, seed: int = 0) -> dict | None:
     }
 
 
+def torch_index_topk(q_idx, k_idx, topk: int, block: int, softmax: bool = True, chunk: int = 2048,
+                     score_dtype=None, pooled_out=None):
+    """Index top-k the plain PyTorch way, for the comparison with the fused
+    kernel: materialise the causal index scores of a chunk of queries
+    (q_idx k_idx^T over the visible keys), max-pool them per block, optionally
+    take the softmax over the visible blocks, force each query's own block and
+    call torch.topk.  Returns block_idx [B,N,H_kv,topk] int32, ascending, -1
+    padded, like msa_index_topk.  score_dtype: dtype of the score product
+    (default: the inputs' dtype, as torch.matmul does).  pooled_out: optional
+    fp32 [B,N,H_kv,N/block] that receives the pooled scores (-inf where
+    invisible, own block not forced)."""
+    import torch
+    B, N, H_kv, di = q_idx.shape
+    dev = q_idx.device
+    out = torch.full((B, N, H_kv, topk), -1, dtype=torch.int32, device=dev)
+    ar = torch.arange(N, device=dev)
+    big = torch.iinfo(torch.int32).max
+    for b in range(B):
+        kt = k_idx[b].t().contiguous()                              # [d_idx, N]
+        if score_dtype is not None:
+            kt = kt.to(score_dtype)
+        for c0 in range(0, N, chunk):
+            c1 = min(N, c0 + chunk)
+            C, nb = c1 - c0, (c1 + block - 1) // block               # blocks visible to the chunk
+            U = nb * block
+            q = q_idx[b, c0:c1].reshape(C * H_kv, di)
+            if score_dtype is not None:
+                q = q.to(score_dtype)
+            r = torch.matmul(q, kt[:, :U].contiguous()).view(C, H_kv, U).float()
+            r.masked_fill_(ar[:U].view(1, 1, U) > ar[c0:c1].view(C, 1, 1), float("-inf"))
+            pooled = r.view(C, H_kv, nb, block).amax(-1)           # [C, H_kv, nb]; -inf where invisible
+            if pooled_out is not None:
+                pooled_out[b, c0:c1, :, :nb] = pooled
+                pooled_out[b, c0:c1, :, nb:] = float("-inf")
+            if softmax:
+                pooled = torch.softmax(pooled, dim=-1)              # invisible blocks -> 0
+                pooled = torch.where(torch.isfinite(r.view(C, H_kv, nb, block)[..., 0]), pooled,
+                                     torch.full_like(pooled, -1.0))
+            own = (ar[c0:c1] // block).view(C, 1, 1).expand(C, H_kv, 1)
+            pooled.scatter_(2, own, float("inf"))
+            k = min(topk, nb)
+            val, idx = torch.topk(pooled, k, dim=-1)
+            invisible = (val < 0) if softmax else torch.isinf(val) & (val < 0)
+            idx = torch.where(invisible, torch.full_like(idx, big), idx)
+            idx = torch.sort(idx, dim=-1).values
+            idx = torch.where(idx == big, torch.full_like(idx, -1), idx)
+            out[b, c0:c1, :, :k] = idx.to(torch.int32)
+    return out
+
+
+def compare_topk(args) -> int:
+    """Fused index top-k against the materialise-then-torch.topk pipeline on
+    the index inputs of `args.workload`: one JSON line with both times."""
+    import torch
+    import block_sparse_attention_branch_amd as msa
+    import msa_inputs
+    msa.load_library()
+    w = msa_inputs.WORKLOADS[args.workload]
+    x = msa_inputs.make_inputs(w, args.variant, device="cuda")
+    qi, ki = x["q_idx"], x["k_idx"]
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            res = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, res
+
+    ours_ms, sel = timed(lambda: msa.index_topk(qi, ki, topk=w.topk, block_size=w.block_size, causal=True), 10)
+    soft_ms, ref_soft = timed(lambda: torch_index_topk(qi, ki, w.topk, w.block_size, softmax=True), 3)
+    raw_ms, ref_raw = timed(lambda: torch_index_topk(qi, ki, w.topk, w.block_size, softmax=False), 3)
+    agree = float((torch.sort(sel, dim=-1).values == torch.sort(ref_raw, dim=-1).values).all(-1).float().mean())
+    # The top-k stage alone on materialised pooled scores (what an exp-free
+    # top-k replaces): softmax over the visible blocks (or none), own block
+    # forced, torch.topk.  The fused kernel above also forms the scores.
+    nblk = w.N // w.block_size
+    pooled = torch.empty(w.B, w.N, w.H_kv, nblk, dtype=torch.float32, device="cuda")
+    torch_index_topk(qi, ki, w.topk, w.block_size, softmax=False, pooled_out=pooled)
+    own = (torch.arange(w.N, device="cuda") // w.block_size).view(1, w.N, 1, 1).expand(w.B, w.N, w.H_kv, 1)
+
+    def stage(softmax):
+        p = torch.softmax(pooled, dim=-1) if softmax else pooled.clone()
+        p.scatter_(3, own, 2.0 if softmax else float("inf"))
+        return torch.topk(p, w.topk, dim=-1)
+
+    stage_soft_ms, _ = timed(lambda: stage(True), 3)
+    stage_raw_ms, _ = timed(lambda: stage(False), 3)
+    del pooled
+    line = {"metric": "index top-k ms (fused kernel vs materialise + torch.topk)", "workload": w.name,
+            "config": {"B": w.B, "N": w.N, "H_kv": w.H_kv, "d_idx": w.d_idx, "block_size": w.block_size,
+                       "topk": w.topk, "dtype": w.dtype},
+            "fused_ms": ours_ms, "torch_softmax_topk_ms": soft_ms, "torch_topk_ms": raw_ms,
+            "speedup_vs_softmax_topk": soft_ms / ours_ms, "speedup_vs_topk": raw_ms / ours_ms,
+            "topk_stage_softmax_ms": stage_soft_ms, "topk_stage_ms": stage_raw_ms,
+            "speedup_vs_topk_stage_softmax": stage_soft_ms / ours_ms,
+            "rows_identical_to_torch_topk": agree,
+            "note": "torch pipeline: bf16 score product per 2048-query chunk over the visible keys, causal mask, "
+                    "block max-pool, (softmax), own block forced, torch.topk, sort; topk_stage_*: softmax (or "
+                    "none) + own block + torch.topk on the materialised fp32 pooled scores [B,N,H_kv,N/128]"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +311,9 @@ def main() -> int:
                          "taken with --copy-mib, into profiles/traffic_<kernel>_<workload>.json")
     ap.add_argument("--traffic-kernel", default="bwd_main")
     ap.add_argument("--traffic-command", default="", help="the rocprofv3 command the CSVs came from (recorded)")
+    ap.add_argument("--compare-topk", action="store_true",
+                    help="time the fused index top-k against a materialise + torch.topk pipeline (index inputs "
+                         "of --workload) and print one JSON line")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -223,6 +334,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.compare_topk:
+        return compare_topk(args)
     msa.load_library()
     w = msa_inputs.WORKLOADS[args.workload]
     x = msa_inputs.make_inputs(w, args.variant, device="cuda")
