@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MSA fwd+bwd tokens/s at N=128K; sparse-attn TFLOP/s as % of bf16 MFMA peak"
 
@@ -295,6 +296,45 @@ def compare_topk(args) -> int:
     return 0
 
 
+def index_only(args) -> int:
+    """The index branch alone (msa_index_topk) on the index inputs of
+    `args.workload`, with bf16 and with FP8 E4M3 inputs: one JSON line with
+    each kernel's time (library hipEvents) and its rate against its dtype's
+    dense MFMA peak."""
+    import torch
+    import block_sparse_attention_branch_amd as msa
+    import msa_inputs
+    msa.load_library()
+    w = msa_inputs.WORKLOADS[args.workload]
+    flop = algorithmic_work(w)["index_topk"][1]
+    res = {}
+    for name, fp8, peak in (("bf16", False, PEAK_BF16_TFLOPS), ("fp8_e4m3", True, PEAK_FP8_TFLOPS)):
+        x = msa_inputs.make_inputs(w, args.variant, device="cuda", index_fp8=fp8)
+        qi, ki = x["q_idx"], x["k_idx"]
+        del x
+        for _ in range(args.warmup):
+            msa.index_topk(qi, ki, topk=w.topk, block_size=w.block_size, causal=w.causal)
+        torch.cuda.synchronize()
+        msa.profile_enable(True)
+        msa.profile_collect()
+        for _ in range(args.steps):
+            msa.index_topk(qi, ki, topk=w.topk, block_size=w.block_size, causal=w.causal)
+        torch.cuda.synchronize()
+        launches, total_ms = msa.profile_collect()["index_topk"]
+        msa.profile_enable(False)
+        ms = total_ms / launches
+        tf = flop / (ms * 1e-3) / 1e12
+        res[name] = {"ms": ms, "achieved": tf, "unit": "TFLOP/s", "peak": peak, "frac": tf / peak}
+        del qi, ki
+        torch.cuda.empty_cache()
+    line = {"metric": "index top-k (scores + block max-pool + top-k) ms and MFMA rate", "workload": w.name,
+            "config": {"B": w.B, "N": w.N, "H_kv": w.H_kv, "d_idx": w.d_idx, "block_size": w.block_size,
+                       "topk": w.topk}, "flop_per_launch": flop, "steps": args.steps, "warmup": args.warmup,
+            "kernels": res, "fp8_speedup": res["bf16"]["ms"] / res["fp8_e4m3"]["ms"]}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +354,8 @@ def main() -> int:
     ap.add_argument("--compare-topk", action="store_true",
                     help="time the fused index top-k against a materialise + torch.topk pipeline (index inputs "
                          "of --workload) and print one JSON line")
+    ap.add_argument("--index-only", action="store_true",
+                    help="time msa_index_topk alone with bf16 and with FP8 E4M3 index inputs of --workload")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -336,6 +378,8 @@ def main() -> int:
         return 1
     if args.compare_topk:
         return compare_topk(args)
+    if args.index_only:
+        return index_only(args)
     msa.load_library()
     w = msa_inputs.WORKLOADS[args.workload]
     x = msa_inputs.make_inputs(w, args.variant, device="cuda")

@@ -24,6 +24,7 @@ MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
 MSA_F32 = 0
 MSA_BF16 = 1
+MSA_FP8_E4M3 = 2   # index inputs of msa_index_topk only
 
 EXPORTED = (
     "msa_index_topk_workspace", "msa_index_topk",
@@ -105,6 +106,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return MSA_BF16
     if t.dtype == torch.float32:
         return MSA_F32
+    if t.dtype == torch.float8_e4m3fn:
+        return MSA_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -133,7 +136,8 @@ def _workspace(nbytes: int, device):
 
 def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int = 16, block_size: int = 128,
                causal: bool = True, return_pooled: bool = False):
-    """block_idx [B,N,H_kv,topk] int32 (and pooled [B,N,H_kv,N/block_size] fp32)."""
+    """block_idx [B,N,H_kv,topk] int32 (and pooled [B,N,H_kv,N/block_size] fp32).
+    q_idx, k_idx: bf16, fp32, or float8_e4m3fn (d_idx = 64) for the FP8 indexer."""
     lib = load_library()
     _need(q_idx, "q_idx")
     _need(k_idx, "k_idx", q_idx.dtype)

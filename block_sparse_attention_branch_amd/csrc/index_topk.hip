@@ -269,6 +269,7 @@ hipError_t launch_index_topk(const Problem& P, const void* q_idx, const void* k_
     hipError_t e = launch_fill_f32(pooled, (size_t)P.B * P.N * P.H_kv * P.nblk, -INFINITY, s);
     if (e != hipSuccess) return e;
   }
+  if (P.dtype == MSA_FP8_E4M3) return launch_cap<fp8e4m3, 64>(P, q_idx, k_idx, block_idx, pooled, s);
   if (P.dtype == MSA_BF16) {
     if (P.d_idx == 64) return launch_cap<bf16, 64>(P, q_idx, k_idx, block_idx, pooled, s);
     return launch_cap<bf16, 32>(P, q_idx, k_idx, block_idx, pooled, s);

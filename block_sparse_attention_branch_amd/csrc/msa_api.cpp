@@ -51,7 +51,7 @@ int check_dims(const msa_dims* d, msa::Problem* P) {
   if (d->H_q % d->H_kv != 0)
     return fail(MSA_ERR_INVALID_ARG, "H_q=%d is not a multiple of H_kv=%d", d->H_q, d->H_kv);
   if (d->causal != 0 && d->causal != 1) return fail(MSA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (d->dtype != MSA_F32 && d->dtype != MSA_BF16)
+  if (d->dtype != MSA_F32 && d->dtype != MSA_BF16 && d->dtype != MSA_FP8_E4M3)
     return fail(MSA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
   if (!std::isfinite(d->scale) || d->scale < 0.f || !std::isfinite(d->scale_idx) || d->scale_idx < 0.f)
     return fail(MSA_ERR_INVALID_ARG, "scale and scale_idx must be finite and >= 0");
@@ -80,6 +80,13 @@ int check_dims(const msa_dims* d, msa::Problem* P) {
   P->nblk = d->N / msa::kBlock;
   P->scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->d);
   P->scale_idx = d->scale_idx > 0.f ? d->scale_idx : 1.0f / std::sqrt((float)d->d_idx);
+  return MSA_OK;
+}
+
+// The main branch takes fp32 or bf16; FP8 is an index-branch format only.
+int check_main_dtype(const msa::Problem& P) {
+  if (P.dtype == MSA_FP8_E4M3)
+    return fail(MSA_ERR_UNSUPPORTED, "dtype FP8 E4M3 is accepted by msa_index_topk only");
   return MSA_OK;
 }
 
@@ -234,6 +241,8 @@ MSA_API int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* 
   msa::Problem P;
   int st = check_dims(dims, &P);
   if (st != MSA_OK) return st;
+  if (P.dtype == MSA_FP8_E4M3 && P.d_idx != 64)
+    return fail(MSA_ERR_UNSUPPORTED, "FP8 E4M3 index inputs need d_idx=64 (got %d)", P.d_idx);
   REQUIRE(q_idx);
   REQUIRE(k_idx);
   REQUIRE(block_idx);
@@ -246,7 +255,7 @@ MSA_API int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* 
 
 MSA_API size_t msa_sparse_fwd_workspace(const msa_dims* dims) {
   msa::Problem P;
-  if (check_dims(dims, &P) != MSA_OK) return 0;
+  if (check_dims(dims, &P) != MSA_OK || check_main_dtype(P) != MSA_OK) return 0;
   return align_up(msa::block_map_bytes(P)) + align_up(msa::sparse_fwd_partials_bytes(P, fwd_chunk_queries(P)));
 }
 
@@ -256,6 +265,7 @@ MSA_API int msa_sparse_fwd(const msa_dims* dims, const void* q, const void* k, c
   msa::Problem P;
   int st = check_dims(dims, &P);
   if (st != MSA_OK) return st;
+  if ((st = check_main_dtype(P)) != MSA_OK) return st;
   REQUIRE(q);
   REQUIRE(k);
   REQUIRE(v);
@@ -279,7 +289,7 @@ MSA_API int msa_sparse_fwd(const msa_dims* dims, const void* q, const void* k, c
 
 MSA_API size_t msa_sparse_bwd_workspace(const msa_dims* dims) {
   msa::Problem P;
-  if (check_dims(dims, &P) != MSA_OK) return 0;
+  if (check_dims(dims, &P) != MSA_OK || check_main_dtype(P) != MSA_OK) return 0;
   if (P.dtype != MSA_BF16) return 0;
   return align_up(msa::block_map_bytes(P)) + align_up(msa::sparse_bwd_scratch_bytes(P));
 }
@@ -293,6 +303,7 @@ MSA_API int msa_sparse_bwd(const msa_dims* dims, const void* q, const void* k, c
   msa::Problem P;
   int st = check_dims(dims, &P);
   if (st != MSA_OK) return st;
+  if ((st = check_main_dtype(P)) != MSA_OK) return st;
   REQUIRE(q);
   REQUIRE(k);
   REQUIRE(v);

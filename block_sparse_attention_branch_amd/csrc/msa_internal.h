@@ -41,6 +41,31 @@ template <> struct Mma<bf16> {
   }
 };
 
+// One OCP FP8 E4M3 value (the element type of FP8 index inputs).
+struct fp8e4m3 {
+  uint8_t bits;
+};
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// gfx950 FP8 matrix unit, 32x32x64 per instruction: lane l holds 32
+// consecutive k values of row (A) or column (B) l % 32, the half of k chosen
+// by l / 32, as for the other 32x32 forms; both operands E4M3 (format code 0)
+// with unit block scales (E8M0 exponent 127).
+template <> struct Mma<fp8e4m3> {
+  typedef i32x8 frag;
+  static constexpr int KPL = 32;
+  __device__ static inline frag load(const fp8e4m3* p) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(p);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+    frag r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+  }
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
 template <> struct Mma<float> {
   typedef float frag;
   static constexpr int KPL = 1;

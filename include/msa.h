@@ -64,8 +64,11 @@ enum {
   MSA_ERR_HIP = -4           /* a HIP launch failed (see msa_last_error) */
 };
 
-/* Element types. */
-enum { MSA_F32 = 0, MSA_BF16 = 1 };
+/* Element types.  MSA_FP8_E4M3 is the OCP 8-bit float E4M3 in its finite
+ * form (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities;
+ * codes 0x7F and 0xFF are NaN).  It is accepted by msa_index_topk only: the
+ * indexer in a lighter format, [MSA] "Kernel optimizations". */
+enum { MSA_F32 = 0, MSA_BF16 = 1, MSA_FP8_E4M3 = 2 };
 
 /* Problem description, passed by pointer to every call. */
 typedef struct msa_dims {
@@ -78,7 +81,8 @@ typedef struct msa_dims {
   int32_t block_size; /* tokens per KV block (128 on the pages) */
   int32_t topk;       /* blocks kept per query and group (16 on the pages) */
   int32_t causal;     /* 1: query t sees keys u <= t; 0: sees every key */
-  int32_t dtype;      /* MSA_F32 or MSA_BF16 */
+  int32_t dtype;      /* element type of the call's floating inputs: MSA_F32 or
+                         MSA_BF16; msa_index_topk also takes MSA_FP8_E4M3 */
   float scale;        /* main-branch score scale; 0 selects 1/sqrt(d) */
   float scale_idx;    /* index-logit scale of the KL student; 0 selects 1/sqrt(d_idx) */
 } msa_dims;
@@ -104,6 +108,10 @@ typedef struct msa_dims {
  *                   blocks.  Meant for tests: it costs an extra N^2/128 write.
  * Scores accumulate in fp32; for integer-valued inputs they are exact, so
  * block_idx is reproducible bit for bit.
+ * dtype MSA_FP8_E4M3 (d_idx = 64 only): q_idx and k_idx are E4M3 bytes and
+ * the products run on the FP8 matrix unit, accumulating in fp32.  A product
+ * of two E4M3 values is exact in fp32, so the same holds for integer-valued
+ * inputs.  NaN codes give an unspecified selection.
  */
 MSA_API size_t msa_index_topk_workspace(const msa_dims* dims);
 MSA_API int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx,

@@ -88,12 +88,14 @@ def _draw(shape, gen, device, variant):
 
 
 def make_inputs(w: Workload, variant: str = "normal", seed: int | None = None,
-                device="cpu", with_grad_out: bool | None = None) -> dict:
+                device="cpu", with_grad_out: bool | None = None, index_fp8: bool = False) -> dict:
     """Build the workload's tensors on `device` from a fixed seed.
 
     Returns q [B,N,H_q,d], k, v [B,N,H_kv,d], q_idx [B,N,H_kv,d_idx],
     k_idx [B,N,d_idx] in the workload dtype, plus dO [B,N,H_q,d] when the
-    workload has a backward (or when asked)."""
+    workload has a backward (or when asked).  index_fp8: q_idx and k_idx are
+    instead rounded from the same fp32 draws to float8_e4m3fn (torch's cast,
+    round to nearest even)."""
     if variant not in VARIANT_SEED_OFFSET:
         raise ValueError(f"unknown variant {variant!r}")
     seed = (w.seed + VARIANT_SEED_OFFSET[variant]) if seed is None else seed
@@ -118,8 +120,9 @@ def make_inputs(w: Workload, variant: str = "normal", seed: int | None = None,
         blk = torch.arange(w.N, device=device) // w.block_size
         planted = (blk % PLANT_EVERY == 0).to(torch.float32)
         ki = ki + PLANT_BETA * planted[None, :, None] * c
-    out["q_idx"] = qi.to(dt)
-    out["k_idx"] = ki.to(dt)
+    idt = torch.float8_e4m3fn if index_fp8 else dt
+    out["q_idx"] = qi.to(idt)
+    out["k_idx"] = ki.to(idt)
     return out
 
 

@@ -182,6 +182,26 @@ def index_topk(q_idx: np.ndarray, k_idx: np.ndarray, block_size: int, topk: int,
 
 
 # --------------------------------------------------------------------------
+# FP8 E4M3 index inputs ([MSA] "Kernel optimizations": a lighter indexer
+# format).  The index branch is then the same definition over the decoded
+# values; only the decoding is new.
+# --------------------------------------------------------------------------
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (the finite form: 1 sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN), as
+    float64: exponent field 0 is subnormal, m / 8 * 2^-6; otherwise
+    (1 + m / 8) * 2^(e - 7)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, out)
+
+
+# --------------------------------------------------------------------------
 # A5: exact softmax attention over the selected support, with LSE.
 # --------------------------------------------------------------------------
 

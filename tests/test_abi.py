@@ -138,3 +138,20 @@ def test_fp32_backward_unsupported(lib):
     st = lib.msa_sparse_bwd(d, *([FAKE] * 9), 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE,
                             1 << 40, NULL)
     assert st == bnd.MSA_ERR_UNSUPPORTED
+
+
+def test_fp8_only_for_the_index_branch(lib):
+    d8 = good_dims(dtype=bnd.MSA_FP8_E4M3)
+    st = lib.msa_sparse_fwd(ctypes.byref(d8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL)
+    assert st == bnd.MSA_ERR_UNSUPPORTED
+    st = lib.msa_sparse_bwd(ctypes.byref(d8), *([FAKE] * 9), 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE,
+                            1 << 40, NULL)
+    assert st == bnd.MSA_ERR_UNSUPPORTED
+    assert lib.msa_sparse_fwd_workspace(ctypes.byref(d8)) == 0
+    assert lib.msa_sparse_bwd_workspace(ctypes.byref(d8)) == 0
+    # The FP8 indexer is built for d_idx = 64; other index dims are refused.
+    d32 = good_dims(dtype=bnd.MSA_FP8_E4M3, d_idx=32)
+    assert lib.msa_index_topk(ctypes.byref(d32), FAKE, FAKE, FAKE, NULL, NULL, 0, NULL) == bnd.MSA_ERR_UNSUPPORTED
+    assert lib.msa_index_topk(ctypes.byref(d8), NULL, FAKE, FAKE, NULL, NULL, 0, NULL) == bnd.MSA_ERR_INVALID_ARG
+    bad = good_dims(dtype=7)
+    assert lib.msa_index_topk(ctypes.byref(bad), FAKE, FAKE, FAKE, NULL, NULL, 0, NULL) == bnd.MSA_ERR_INVALID_ARG

@@ -17,18 +17,26 @@ from tests.gpu_helpers import (f32, need_gpu, row_tolerance, sample_rows, say, s
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, variant, want_pooled=True, causal=True):
+def _host(t: torch.Tensor):
+    """Exact host values of index inputs: FP8 E4M3 through the oracle's own
+    decoding of the bytes, other dtypes by an exact upcast."""
+    if t.dtype == torch.float8_e4m3fn:
+        return O.decode_e4m3(t.view(torch.uint8).cpu().numpy())
+    return f32(t)
+
+
+def _run(w, variant, want_pooled=True, causal=True, fp8=False):
     msa = need_gpu()
-    say(f"[index] {w.name} variant={variant} causal={causal} N={w.N} H_kv={w.H_kv} topk={w.topk}")
-    x = msa_inputs.make_inputs(w, variant, device="cuda")
+    say(f"[index] {w.name} variant={variant} causal={causal} N={w.N} H_kv={w.H_kv} topk={w.topk} fp8={fp8}")
+    x = msa_inputs.make_inputs(w, variant, device="cuda", index_fp8=fp8)
     out = msa.index_topk(x["q_idx"], x["k_idx"], topk=w.topk, causal=causal, return_pooled=want_pooled)
     torch.cuda.synchronize()
     return x, out
 
 
-def _check_full(w, variant, causal=True, exact=True):
-    x, (sel, pooled) = _run(w, variant, True, causal)
-    qi, ki = f32(x["q_idx"]), f32(x["k_idx"])
+def _check_full(w, variant, causal=True, exact=True, fp8=False):
+    x, (sel, pooled) = _run(w, variant, True, causal, fp8)
+    qi, ki = _host(x["q_idx"]), _host(x["k_idx"])
     ref_sel, ref_pool = O.index_topk(qi, ki, w.block_size, w.topk, causal=causal, want_pooled=True)
     gsel = sel.cpu().numpy().astype(np.int64)
     gpool = pooled.cpu().numpy()
@@ -108,16 +116,16 @@ def test_bf16_normal_8k():
     _check_full(msa_inputs.WORKLOADS["fwd-bf16-n8k"], "normal", exact=False)
 
 
-def _sampled(w, variant, n_rows, seed):
+def _sampled(w, variant, n_rows, seed, fp8=False):
     msa = need_gpu()
-    say(f"[index sampled] {w.name} variant={variant}")
-    x = msa_inputs.make_inputs(w, variant, device="cuda")
+    say(f"[index sampled] {w.name} variant={variant} fp8={fp8}")
+    x = msa_inputs.make_inputs(w, variant, device="cuda", index_fp8=fp8)
     sel = msa.index_topk(x["q_idx"], x["k_idx"], topk=w.topk)
     torch.cuda.synchronize()
     rows = sample_rows(w.B, w.N, n_rows, seed)
     bt = torch.tensor(rows, dtype=torch.long)
-    qi_rows = f32(x["q_idx"][bt[:, 0], bt[:, 1]])
-    ki = f32(x["k_idx"])
+    qi_rows = _host(x["q_idx"][bt[:, 0], bt[:, 1]])
+    ki = _host(x["k_idx"])
     ref_sel, ref_pool = O.index_topk(qi_rows, ki, w.block_size, w.topk, rows=rows, want_pooled=True)
     gsel = sel[bt[:, 0], bt[:, 1]].cpu().numpy().astype(np.int64)
     flagged = 0
@@ -158,6 +166,30 @@ def test_bf16_128k_planted_closed_form():
 
 def test_bf16_1m_sampled():
     _sampled(msa_inputs.WORKLOADS["fwdbwd-bf16-n1m"], "normal", 32, 5)
+
+
+# FP8 E4M3 index inputs (d_idx = 64): the same bar, with the oracle run on the
+# decoded E4M3 values.  Products of E4M3 values are exact in fp32, so integer
+# inputs give exact scores and bit-exact pooled scores and selections.
+def test_fp8_integer_inputs_bit_exact():
+    w = msa_inputs.Workload("fp8-int-4k", B=2, N=4096, H_q=8, H_kv=8, d=128, d_idx=64, topk=16, seed=121)
+    _check_full(w, "int", exact=True, fp8=True)
+
+
+@pytest.mark.parametrize("topk", [1, 5, 32])
+def test_fp8_integer_topk_edges_and_noncausal(topk):
+    w = msa_inputs.Workload(f"fp8-int-k{topk}", B=1, N=2048, H_q=6, H_kv=3, d=64, d_idx=64, topk=topk,
+                            seed=130 + topk)
+    _check_full(w, "int", exact=True, fp8=True)
+    _check_full(w, "int", causal=False, exact=True, fp8=True)
+
+
+def test_fp8_normal_8k():
+    _check_full(msa_inputs.WORKLOADS["fwd-bf16-n8k"], "normal", exact=False, fp8=True)
+
+
+def test_fp8_128k_sampled():
+    _sampled(msa_inputs.WORKLOADS["fwd-bf16-n128k"], "normal", 96, 14, fp8=True)
 
 
 @pytest.mark.parametrize("softmax", [False, True])
