@@ -668,8 +668,12 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     peek(st + 2);
     if (st > 0) dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
 
+    // The two product stretches of the step run at raised wave priority: of
+    // two waves of a SIMD in the same stretch, one then runs ahead and reaches
+    // its vector work while the other still issues products.
     // S, dP (two row tiles) and the index logits (NTQ query-row tiles): lane
     // = key, slots = rows.
+    __builtin_amdgcn_s_setprio(1);
     f32x4 s[2], dp[2], ri[NTQ];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -692,6 +696,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
                       *reinterpret_cast<const bf16x8*>(KIs + C::TI::off(key, col)), ri[t]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // P, dS; dS^T to LDS (rows 16 t + 4 lq .. +3 of this lane's key).
     f32x4 p[2], ds[2];
 #pragma unroll
@@ -748,6 +753,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     // dV^T += dO^T P, dK^T += Q^T dS (K = the 32 rows, in the order of the
     // two tiles' slots), dk_idx^T += q_idx^T dz.
     {
+      __builtin_amdgcn_s_setprio(1);
       const bf16x8 pbf = cpair(p[0], p[1]), sbf = cpair(ds[0], ds[1]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -758,6 +764,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 #pragma unroll
       for (int dt = 0; dt < DTI; ++dt)
         acc_dki[dt] = mma16(tr16<typename C::TI>(QIs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), zb, acc_dki[dt]);
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();   // dS^T, dz^T and the KL partials complete
 
@@ -814,57 +821,65 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 // partials over the valid slots of its selection (one partial per selected
 // block, written by the main kernel; layout [b, query, slot, head, d], so the
 // heads of one query and slot are contiguous on both sides).  D / 8 lanes per
-// row, 16 bytes each; the partials are read 8 slots at a time with all 8 loads
-// in flight.  Padded slots hold unwritten memory and are excluded by selection.
-template <int D>
+// row, 16 bytes each.  KM >= topk is the compile-time slot count: all partial
+// loads of the row are issued at once (slot indices past topk clamped to the
+// last slot and skipped), so a row costs one memory round trip.  Padded slots
+// hold unwritten memory and are excluded by selection.  Row indices fit in 32
+// bits (checked by the host).
+template <int D, int KM>
 __global__ __launch_bounds__(256) void dq_merge_kernel(const bf16* __restrict__ part,
                                                        const int32_t* __restrict__ block_idx, bf16* __restrict__ dq,
                                                        int B, int N, int H_kv, int G, int topk, int c0, int CQ) {
   constexpr int LPR = D / 8;
-  constexpr int MAXK = 32, CH = 8;
   const int H_q = H_kv * G;
-  const size_t row = (size_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  if (row >= (size_t)B * CQ * H_q) return;
+  const int row = blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  if (row >= B * CQ * H_q) return;
   const int col = (threadIdx.x % LPR) * 8;
-  const int h = (int)(row % H_q);
-  const size_t bt = row / H_q;
-  const int tl = (int)(bt % CQ), b = (int)(bt / CQ);
+  const int h = row % H_q;
+  const int bt = row / H_q;
+  const int tl = bt % CQ, b = bt / CQ;
   const int t = c0 + tl, g = h / G;
   const int32_t* brow = block_idx + (((size_t)b * N + t) * H_kv + g) * topk;
-  bool ok[MAXK];
+  const bf16* prow = part + ((size_t)bt * topk * H_q + h) * D + col;   // slot e at + e H_q D
+  bf16x8 raw[KM];
 #pragma unroll
-  for (int e = 0; e < MAXK; ++e) ok[e] = false;
-  if ((topk & 3) == 0) {
+  for (int e = 0; e < KM; ++e) raw[e] = *reinterpret_cast<const bf16x8*>(prow + (size_t)min(e, topk - 1) * H_q * D);
+  bool ok[KM];
+  if (topk == KM) {
 #pragma unroll
-    for (int e = 0; e < MAXK; e += 4)
-      if (e < topk) {
-        const int4 bi = *reinterpret_cast<const int4*>(brow + e);
-        ok[e] = bi.x >= 0; ok[e + 1] = bi.y >= 0; ok[e + 2] = bi.z >= 0; ok[e + 3] = bi.w >= 0;
-      }
+    for (int e = 0; e < KM; e += 4) {
+      const int4 bi = *reinterpret_cast<const int4*>(brow + e);
+      ok[e] = bi.x >= 0; ok[e + 1] = bi.y >= 0; ok[e + 2] = bi.z >= 0; ok[e + 3] = bi.w >= 0;
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < MAXK; ++e)
-      if (e < topk) ok[e] = brow[e] >= 0;
+    for (int e = 0; e < KM; ++e) ok[e] = e < topk && brow[min(e, topk - 1)] >= 0;
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const bf16* prow = part + (bt * topk * H_q + h) * D + col;   // slot e at + e H_q D
 #pragma unroll
-  for (int e0 = 0; e0 < MAXK; e0 += CH) {
-    if (e0 >= topk) break;
-    bf16x8 raw[CH];
+  for (int e = 0; e < KM; ++e)
+    if (ok[e])
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      if (e0 + i < topk) raw[i] = *reinterpret_cast<const bf16x8*>(prow + (size_t)(e0 + i) * H_q * D);
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-      if (e0 + i < topk && ok[e0 + i])
-#pragma unroll
-        for (int k2 = 0; k2 < 8; ++k2) acc[k2] += (float)raw[i][k2];
-  }
+      for (int k2 = 0; k2 < 8; ++k2) acc[k2] += (float)raw[e][k2];
   bf16x8 y;
 #pragma unroll
   for (int k2 = 0; k2 < 8; ++k2) y[k2] = (bf16)acc[k2];
   *reinterpret_cast<bf16x8*>(dq + (((size_t)b * N + t) * H_q + h) * D + col) = y;
+}
+
+template <int D>
+hipError_t launch_dq_merge(const Problem& P, const bf16* part, const int32_t* block_idx, bf16* dq, int c0, int CQ,
+                           hipStream_t s) {
+  const size_t rows = (size_t)P.B * CQ * P.H_q;
+  if (rows > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int rpb = 256 / (D / 8);
+  const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
+  auto kern = P.topk <= 4 ? dq_merge_kernel<D, 4>
+            : P.topk <= 8 ? dq_merge_kernel<D, 8>
+            : P.topk <= 16 ? dq_merge_kernel<D, 16> : dq_merge_kernel<D, 32>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, part, block_idx, dq, P.B, P.N, P.H_kv, P.G, P.topk, c0,
+                     CQ);
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst,
@@ -1030,18 +1045,11 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
     else e = run_main_g<64, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
     prof_end(s);
     if (e != hipSuccess) return e;
-    const size_t rows = (size_t)P.B * CQ * P.H_q;
-    const int rpb = 256 / (P.d / 8);
-    const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
     prof_begin("bwd_dq_merge", s);
-    if (P.d == 128)
-      hipLaunchKernelGGL(dq_merge_kernel<128>, dim3(blocks), dim3(256), 0, s, w.dq_part, a.block_idx,
-                         static_cast<bf16*>(a.dq), P.B, P.N, P.H_kv, P.G, P.topk, c0, CQ);
-    else
-      hipLaunchKernelGGL(dq_merge_kernel<64>, dim3(blocks), dim3(256), 0, s, w.dq_part, a.block_idx,
-                         static_cast<bf16*>(a.dq), P.B, P.N, P.H_kv, P.G, P.topk, c0, CQ);
+    e = P.d == 128 ? launch_dq_merge<128>(P, w.dq_part, a.block_idx, static_cast<bf16*>(a.dq), c0, CQ, s)
+                   : launch_dq_merge<64>(P, w.dq_part, a.block_idx, static_cast<bf16*>(a.dq), c0, CQ, s);
     prof_end(s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
   }
   // fp32 accumulators to bf16 outputs.
   prof_begin("bwd_finalize", s);

@@ -99,7 +99,7 @@ template <> struct Store4<float> {
 };
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
+__global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ rows, const int32_t* __restrict__ tiles,
@@ -167,41 +167,55 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
       ents[i] = r < n_rows ? ent[r / G] : 0;
     }
   }
-#pragma unroll 1
-  for (int r0 = wave * 32, tile = 0; r0 < n_rows; r0 += 128, ++tile) {
-    // Keep the K/V fragment reads inside the loop (re-read from LDS per row
-    // tile) instead of letting them be hoisted into ~256 live registers.
-    asm volatile("" ::: "memory");
+  // Query, slot and validity of this lane's row in the wave's row tile
+  // `tile` (rows r0 = 32 wave + 128 tile ..).
+  auto locate = [&](int r0, int tile, int* t, int* slot, int* h, bool* valid) {
     const int r = r0 + (lane & 31);
-    const int qi = r / G, hh = r % G;
-    bool valid = r < n_rows;
-    int t, slot = 0;
+    const int qi = r / G;
+    *h = g * G + r % G;
+    *valid = r < n_rows;
+    *slot = 0;
     if (diag) {
-      t = j * kBlock + min(qi, kBlock - 1);
-      const int32_t* brow = block_idx + (((size_t)b * N + t) * H_kv + g) * topk;
+      *t = j * kBlock + min(qi, kBlock - 1);
+      const int32_t* brow = block_idx + (((size_t)b * N + *t) * H_kv + g) * topk;
       for (int e = 0; e < topk; ++e)
-        if (brow[e] == j) slot = e;
+        if (brow[e] == j) *slot = e;
     } else {
       int e = ents[0];
 #pragma unroll
       for (int i = 1; i < kTiles; ++i)
         if (tile == i) e = ents[i];
-      t = e >> 6;
-      slot = e & 63;
+      *t = e >> 6;
+      *slot = e & 63;
       // A well-formed map only yields queries of this chunk; anything else is
       // dropped (and clamped for the loads) rather than trusted.
-      if (t < c0 || t >= c1 || slot >= topk) {
-        valid = false;
-        t = c0;
-        slot = 0;
+      if (*t < c0 || *t >= c1 || *slot >= topk) {
+        *valid = false;
+        *t = c0;
+        *slot = 0;
       }
     }
-    const int h = g * G + hh;
-
-    typename M::frag qf[C::KSTEPS];
+  };
+  typename M::frag qn[C::KSTEPS];   // the next row tile's Q fragments, in flight
+  auto load_q = [&](int t, int h) {
     const T* qrow = q + (((size_t)b * N + t) * H_q + h) * D + KPL * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = M::load(qrow + ks * 2 * KPL);
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qn[ks] = M::load(qrow + ks * 2 * KPL);
+  };
+  int nt, nslot, nh;
+  bool nvalid;
+  locate(wave * 32, 0, &nt, &nslot, &nh, &nvalid);
+  if (wave * 32 < n_rows) load_q(nt, nh);
+#pragma unroll 1
+  for (int r0 = wave * 32, tile = 0; r0 < n_rows; r0 += 128, ++tile) {
+    // Keep the K/V fragment reads inside the loop (re-read from LDS per row
+    // tile) instead of letting them be hoisted into ~256 live registers.
+    asm volatile("" ::: "memory");
+    const int t = nt, slot = nslot, h = nh;
+    const bool valid = nvalid;
+    typename M::frag qf[C::KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = qn[ks];
 
     f32x16 s[4];
 #pragma unroll
@@ -235,6 +249,13 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
         lsum += p;
       }
     lsum += swap_half(lsum);
+
+    // The next row tile's queries: located and their Q loads issued here, so
+    // that the O products and partial stores of this tile cover the gather.
+    if (r0 + 128 < n_rows) {
+      locate(r0 + 128, tile + 1, &nt, &nslot, &nh, &nvalid);
+      load_q(nt, nh);
+    }
 
     // P^T as B-operand fragments (the fp32 score tile dies here).
     typename M::frag pf[4][C::KCH];
@@ -293,78 +314,73 @@ __global__ __launch_bounds__(kFwdThreads) void sparse_fwd_kernel(
 }
 
 // Merge the per-block partials of every (query, head) of the chunk: LPR lanes
-// per (query, head) row, 16 bytes of o each.  The slot weights come first
-// (LSE over the valid slots); then the partials are read 8 slots at a time
-// with all 8 loads in flight, so the kernel streams at memory speed instead
-// of waiting on one load per slot.  Padded slots (block index -1) hold
+// per (query, head) row, 16 bytes of o each.  KM >= topk is the compile-time
+// slot count: every partial load of the row is issued up front (slot indices
+// past topk are clamped to the last slot and their weight is zero), together
+// with the row's block indices and slot log-sum-exps, so that a row costs one
+// memory round trip.  The merge: LSE = logsumexp over the valid slots and
+// o = sum_j exp(lse_j - LSE) o_j.  Padded slots (block index -1) hold
 // unwritten memory: they are excluded by selection, never by multiplying
-// with a zero weight.
-template <typename T, int D>
+// with a zero weight.  Row indices fit in 32 bits (checked by the host).
+template <typename T, int D, int KM>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po, const float* __restrict__ plse,
                                                         const int32_t* __restrict__ block_idx, T* __restrict__ o,
                                                         float* __restrict__ lse, int B, int N, int H_kv, int G,
                                                         int topk, int c0, int CQ) {
   constexpr int EPL = 16 / (int)sizeof(T);   // elements per lane
   constexpr int LPR = D / EPL;               // lanes per row
-  constexpr int MAXK = 32;                   // largest supported topk
-  constexpr int CH = 8;                      // slots per batch of loads
   const int H_q = H_kv * G;
-  const size_t row = (size_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  if (row >= (size_t)B * CQ * H_q) return;
+  const int row = blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  if (row >= B * CQ * H_q) return;
   const int part = threadIdx.x % LPR;
-  const int h = (int)(row % H_q);
-  const size_t bt = row / H_q;
-  const int tl = (int)(bt % CQ), b = (int)(bt / CQ);
+  const int h = row % H_q;
+  const int bt = row / H_q;
+  const int tl = bt % CQ, b = bt / CQ;
   const int t = c0 + tl, g = h / G;
   const int32_t* brow = block_idx + (((size_t)b * N + t) * H_kv + g) * topk;
-  const float* lrow = plse + row * topk;
+  const float* lrow = plse + (size_t)row * topk;
+  const T* prow = po + ((size_t)bt * topk * H_q + h) * D + part * EPL;   // slot e at + e H_q D
+  uint4 raw[KM];
+#pragma unroll
+  for (int e = 0; e < KM; ++e) raw[e] = *reinterpret_cast<const uint4*>(prow + (size_t)min(e, topk - 1) * H_q * D);
   // Slot log-sum-exps in log2 units, -inf for padded slots.
-  float lv[MAXK];
+  float lv[KM];
+  if (topk == KM) {
 #pragma unroll
-  for (int e = 0; e < MAXK; ++e) lv[e] = -INFINITY;
-  if ((topk & 3) == 0) {   // rows of 16-byte multiples: vector reads
-#pragma unroll
-    for (int e = 0; e < MAXK; e += 4)
-      if (e < topk) {
-        const int4 bi = *reinterpret_cast<const int4*>(brow + e);
-        const float4 l4 = *reinterpret_cast<const float4*>(lrow + e);
-        lv[e] = bi.x >= 0 ? l4.x * kLog2e : -INFINITY;
-        lv[e + 1] = bi.y >= 0 ? l4.y * kLog2e : -INFINITY;
-        lv[e + 2] = bi.z >= 0 ? l4.z * kLog2e : -INFINITY;
-        lv[e + 3] = bi.w >= 0 ? l4.w * kLog2e : -INFINITY;
-      }
+    for (int e = 0; e < KM; e += 4) {
+      const int4 bi = *reinterpret_cast<const int4*>(brow + e);
+      const float4 l4 = *reinterpret_cast<const float4*>(lrow + e);
+      lv[e] = bi.x >= 0 ? l4.x * kLog2e : -INFINITY;
+      lv[e + 1] = bi.y >= 0 ? l4.y * kLog2e : -INFINITY;
+      lv[e + 2] = bi.z >= 0 ? l4.z * kLog2e : -INFINITY;
+      lv[e + 3] = bi.w >= 0 ? l4.w * kLog2e : -INFINITY;
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < MAXK; ++e)
-      if (e < topk) lv[e] = brow[e] >= 0 ? lrow[e] * kLog2e : -INFINITY;
+    for (int e = 0; e < KM; ++e) {
+      const int ec = min(e, topk - 1);
+      const int bi = brow[ec];
+      const float l = lrow[ec];
+      lv[e] = (e < topk && bi >= 0) ? l * kLog2e : -INFINITY;
+    }
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < MAXK; ++e) mx = fmaxf(mx, lv[e]);   // finite: the own block is always valid
+  for (int e = 0; e < KM; ++e) mx = fmaxf(mx, lv[e]);   // finite: the own block is always valid
   float den = 0.f;
 #pragma unroll
-  for (int e = 0; e < MAXK; ++e) den += __builtin_amdgcn_exp2f(lv[e] - mx);
+  for (int e = 0; e < KM; ++e) den += __builtin_amdgcn_exp2f(lv[e] - mx);
   const float L2 = mx + __builtin_amdgcn_logf(den);   // log2 of the row's total
   float acc[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-  const T* prow = po + (bt * topk * H_q + h) * D + part * EPL;   // slot e at + e H_q D
 #pragma unroll
-  for (int e0 = 0; e0 < MAXK; e0 += CH) {
-    if (e0 >= topk) break;
-    uint4 raw[CH];
+  for (int e = 0; e < KM; ++e) {
+    if (lv[e] != -INFINITY) {
+      const float wgt = __builtin_amdgcn_exp2f(lv[e] - L2);
+      const T* x = reinterpret_cast<const T*>(&raw[e]);
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      if (e0 + i < topk) raw[i] = *reinterpret_cast<const uint4*>(prow + (size_t)(e0 + i) * H_q * D);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int e = e0 + i;
-      if (e < topk && lv[e] != -INFINITY) {
-        const float wgt = __builtin_amdgcn_exp2f(lv[e] - L2);
-        const T* x = reinterpret_cast<const T*>(&raw[i]);
-#pragma unroll
-        for (int c = 0; c < EPL; ++c) acc[c] = fmaf(wgt, to_f32(x[c]), acc[c]);
-      }
+      for (int c = 0; c < EPL; ++c) acc[c] = fmaf(wgt, to_f32(x[c]), acc[c]);
     }
   }
   const float L = L2 * kLn2;
@@ -375,6 +391,21 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po
   const size_t orow = ((size_t)b * N + t) * H_q + h;
   *reinterpret_cast<uint4*>(o + orow * D + part * EPL) = outv;
   if (part == 0) lse[orow] = L;
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_merge(const Problem& P, const T* po, const float* pl, const int32_t* block_idx, T* o,
+                            float* lse, int c0, int CQ, hipStream_t s) {
+  constexpr int LPR = D / (16 / (int)sizeof(T));
+  const size_t rows = (size_t)P.B * CQ * P.H_q;
+  if (rows > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const unsigned blocks = (unsigned)((rows + (256 / LPR) - 1) / (256 / LPR));
+  auto kern = P.topk <= 4 ? fwd_merge_kernel<T, D, 4>
+            : P.topk <= 8 ? fwd_merge_kernel<T, D, 8>
+            : P.topk <= 16 ? fwd_merge_kernel<T, D, 16> : fwd_merge_kernel<T, D, 32>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, po, pl, block_idx, o, lse, P.B, P.N, P.H_kv, P.G,
+                     P.topk, c0, CQ);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int G>
@@ -405,14 +436,10 @@ hipError_t run_fwd(const Problem& P, const T* q, const T* k, const T* v, const i
                        s_hi, c0, c1, n_lists, P.scale);
     prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    constexpr int LPR = D / (16 / (int)sizeof(T));
-    const size_t rows = (size_t)P.B * CQ * P.H_q;
-    const size_t blocks = (rows + (256 / LPR) - 1) / (256 / LPR);
     prof_begin("fwd_merge", s);
-    hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, po, pl, block_idx, o,
-                       lse, P.B, P.N, P.H_kv, P.G, P.topk, c0, CQ);
+    e = launch_fwd_merge<T, D>(P, po, pl, block_idx, o, lse, c0, CQ, s);
     prof_end(s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
