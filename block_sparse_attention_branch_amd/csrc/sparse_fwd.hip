@@ -279,13 +279,15 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
 
     // Partial o of the row (normalised) and its LSE.  Each 32-column slice
     // goes through the wave's LDS staging tile: lane (row, half) writes its
-    // 4 x 4 values, then lane l stores 16 bytes of row l / RPL (+ 32 / SPL..)
-    // so that each store instruction writes whole 64-byte row segments.
+    // 4 x 4 values, then lane l stores 16 bytes of row l / RPL (+ 32 / SPL..).
     const float inv = 1.f / lsum;
     // LSE partials [b, query, head, slot]; output partials [b, query, slot,
-    // head, d], so that the heads of one query and slot are contiguous.
+    // d / 32, head, 32]: the 32-column slices of one query, slot and slice are
+    // contiguous over the group's heads, so a store instruction (whole slices
+    // of consecutive rows, which are the heads of one or two queries) writes
+    // whole cache lines.  sbase: slice-row of (query, slot, slice 0, head).
     const int lrow = valid ? (((b * CQ + (t - c0)) * H_q + h) * topk + slot) : -1;
-    const int prow = valid ? (((b * CQ + (t - c0)) * topk + slot) * H_q + h) : -1;
+    const int sbase = valid ? (((b * CQ + (t - c0)) * topk + slot) * (C::DT * H_q) + h) : -1;
     if (valid && lane < 32) plse[lrow] = m * scale + logf(lsum);
     {
       constexpr int EPC = C::EPC;                 // elements per 16-byte piece
@@ -303,9 +305,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 32 / RPI; ++i) {
           const int rr = i * RPI + lane / PPR, pc = lane % PPR;
-          const int dst_row = __shfl(prow, rr);
+          const int sb = __shfl(sbase, rr);
           const uint4 x = *reinterpret_cast<const uint4*>(ost + rr * C::PO + pc * EPC);
-          if (dst_row >= 0) *reinterpret_cast<uint4*>(po + (size_t)dst_row * D + dt * 32 + pc * EPC) = x;
+          if (sb >= 0) *reinterpret_cast<uint4*>(po + (size_t)(sb + dt * H_q) * 32 + pc * EPC) = x;
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slice read before it is overwritten
       }
@@ -339,10 +341,15 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po
   const int t = c0 + tl, g = h / G;
   const int32_t* brow = block_idx + (((size_t)b * N + t) * H_kv + g) * topk;
   const float* lrow = plse + (size_t)row * topk;
-  const T* prow = po + ((size_t)bt * topk * H_q + h) * D + part * EPL;   // slot e at + e H_q D
+  // Partials [b, query, slot, d / 32, head, 32]: this lane's 16 bytes lie in
+  // slice (part EPL) / 32; slot e is e (D / 32) H_q 32 elements further.
+  constexpr int NS = D / 32;
+  const int col = part * EPL;
+  const T* prow = po + ((size_t)(bt * topk * NS + col / 32) * H_q + h) * 32 + col % 32;
   uint4 raw[KM];
 #pragma unroll
-  for (int e = 0; e < KM; ++e) raw[e] = *reinterpret_cast<const uint4*>(prow + (size_t)min(e, topk - 1) * H_q * D);
+  for (int e = 0; e < KM; ++e)
+    raw[e] = *reinterpret_cast<const uint4*>(prow + (size_t)min(e, topk - 1) * NS * H_q * 32);
   // Slot log-sum-exps in log2 units, -inf for padded slots.
   float lv[KM];
   if (topk == KM) {
