@@ -38,7 +38,9 @@
 namespace msa {
 namespace {
 
-constexpr int kItemQueries = 128;
+// List entries per work item of the index log-sum-exp pass (its diagonal
+// items hold the block's own 128 queries).
+constexpr int kLseItem = 512;
 
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O)
@@ -91,8 +93,8 @@ __device__ inline bool decode_item(const int32_t* __restrict__ tiles, const int3
   if (!it->diag) {
     const int32_t* pb = pos + (size_t)bg * (nsb + 1) * nblk + it->j;
     const int seg1 = pb[(size_t)nsb * nblk];
-    const int e0 = (local - 1) * kItemQueries;
-    it->nq = min(kItemQueries, seg1 - e0);
+    const int e0 = (local - 1) * kLseItem;
+    it->nq = min(kLseItem, seg1 - e0);
     it->ent = rows + (size_t)bg * N * topk + offs[(size_t)bg * (nblk + 1) + it->j] + e0;
   }
   return true;
@@ -148,43 +150,61 @@ __global__ __launch_bounds__(256) void idx_lse_kernel(
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int qi = wave * 32 + (lane & 31);
-  if (wave * 32 >= it.nq) return;
+  // Query tiles of 32: wave w takes tiles w, w + 4, ...; a tile's query ids
+  // and q_idx rows are fetched while the previous tile computes.
+  int tile = wave;
+  if (tile * 32 >= it.nq) return;
   int t, slot;
   bool valid;
-  item_query(it, qi, block_idx, N, H_kv, topk, &t, &slot, &valid);
-  bf16x8 qf[KSTEPS];
-  const bf16* qrow = q_idx + (((size_t)it.b * N + t) * H_kv + it.g) * DIDX + 8 * (lane >> 5);
+  bf16x8 qn[KSTEPS];
+  auto fetch = [&](int tl) {
+    item_query(it, tl * 32 + (lane & 31), block_idx, N, H_kv, topk, &t, &slot, &valid);
+    const bf16* qrow = q_idx + (((size_t)it.b * N + t) * H_kv + it.g) * DIDX + 8 * (lane >> 5);
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
-  f32x16 s[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    s[mt] = zero16();
-    const bf16* kp = Ks + (mt * 32 + (lane & 31)) * PK + 8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + ks * 16), qf[ks],
-                                                       s[mt], 0, 0, 0);
-  }
+    for (int ks = 0; ks < KSTEPS; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+  };
+  fetch(tile);
   const float c = scale_idx * kLog2e;
-  float m = -INFINITY;
+#pragma unroll 1
+  while (true) {
+    const int tc = t, sc = slot;
+    const bool vc = valid;
+    bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = qn[ks];
+    const int next = tile + 4;
+    const bool more = next * 32 < it.nq;
+    if (more) fetch(next);
+    f32x16 s[4];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const bool vis = !(it.diag && causal && it.j * kBlock + mt * 32 + c_row(v, lane) > t);
-      s[mt][v] = vis ? s[mt][v] * c : -INFINITY;
-      m = fmaxf(m, s[mt][v]);
+    for (int mt = 0; mt < 4; ++mt) {
+      s[mt] = zero16();
+      const bf16* kp = Ks + (mt * 32 + (lane & 31)) * PK + 8 * (lane >> 5);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + ks * 16), qf[ks],
+                                                         s[mt], 0, 0, 0);
     }
-  m = fmaxf(m, swap_half(m));
-  float l = 0.f;
+    float m = -INFINITY;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) l += exp2f(s[mt][v] - m);
-  l += swap_half(l);
-  if (valid && lane < 32) part[(((size_t)it.b * N + t) * H_kv + it.g) * topk + slot] = make_float2(m, l);
+      for (int v = 0; v < 16; ++v) {
+        const bool vis = !(it.diag && causal && it.j * kBlock + mt * 32 + c_row(v, lane) > tc);
+        s[mt][v] = vis ? s[mt][v] * c : -INFINITY;
+        m = fmaxf(m, s[mt][v]);
+      }
+    m = fmaxf(m, swap_half(m));
+    float l = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) l += __builtin_amdgcn_exp2f(s[mt][v] - m);
+    l += swap_half(l);
+    if (vc && lane < 32) part[(((size_t)it.b * N + tc) * H_kv + it.g) * topk + sc] = make_float2(m, l);
+    if (!more) break;
+    tile = next;
+  }
 }
 
 // lse_idx (natural log) from the per-slot partials (log2-domain max, sum).
@@ -533,12 +553,21 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   };
   Pre pre;
   int pk_e = -1, pk_qi = -1, pk_qt = -1;
-  auto entry = [&](int qi) { return qi < nq ? qlist[qi] : -1; };
+  // List reads and atomics of a step are unconditional (clamped index, value
+  // selected afterwards), so the step has no branches the scheduler must
+  // respect and the latencies of its phases can overlap.
+  auto entry = [&](int qi) {
+    const int v = qlist[min(qi, kBlock + kBigItem - 1)];
+    return qi < nq ? v : -1;
+  };
   auto cutoff = [&](int qi, int t) { return t < 0 ? -1 : ((qi < it.n_own && causal) ? t : 0x7fffffff); };
   auto peek = [&](int st) {
-    pk_e = ld_row ? entry(st * TQ + ld_rr / G) : -1;
-    pk_qi = (ld_qi && ld_qq >= 0) ? entry(st * TQ + ld_qq) : -1;
-    pk_qt = (tx < 32 && mq_q >= 0) ? entry(st * TQ + mq_q) : -1;
+    const int e0 = entry(st * TQ + ld_rr / G);
+    const int e1 = entry(st * TQ + max(ld_qq, 0));
+    const int e2 = entry(st * TQ + max(mq_q, 0));
+    pk_e = ld_row ? e0 : -1;
+    pk_qi = (ld_qi && ld_qq >= 0) ? e1 : -1;
+    pk_qt = (tx < 32 && mq_q >= 0) ? e2 : -1;
   };
   // Unconditional loads (clamped to a valid row): the compiler counts them.
   auto load_step = [&](int st) {
@@ -622,8 +651,11 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (ri_query<G>(t, lq, e) >= 0) {
+          // A row without a query adds +0 to row 0 (dq_idx never holds -0,
+          // so no bit changes).
           const int id = tb[kQryId * 32 + 16 * t + 4 * lq + e];
-          if ((unsigned)id < (unsigned)n_grows) atomicAdd(dq_idx + (size_t)id * DIDX + 16 * ict + c, o[t][e]);
+          const bool ok = (unsigned)id < (unsigned)n_grows;
+          atomicAdd(dq_idx + (size_t)(ok ? id : 0) * DIDX + 16 * ict + c, ok ? o[t][e] : 0.f);
         }
   };
   // Store step st's dQ rows from its tile in LDS as bf16 partials (one row of
@@ -657,16 +689,23 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   load_step(0);
   store_step(0);
   peek(1);
+  // Step -1's row ids (tables of parity 1): none, so the first step's
+  // dq_idx and dQ stores of "step -1" add +0 to row 0 and write the spare
+  // partial row, and the loop needs no branch on st > 0.
+  if (tx < 32) {
+    tabs[NT + kRowId * 32 + tx] = -1;
+    tabs[NT + kQryId * 32 + tx] = -1;
+  }
 #pragma unroll 1
   for (int st = 0; st < n_steps; ++st) {
     asm volatile("" ::: "memory");
     const int* tb = tabs + (st & 1) * NT;
     const float* tf = reinterpret_cast<const float*>(tb);
     __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T / dz^T complete
-    if (st > 0) dq_idx_step(st - 1);
+    dq_idx_step(st - 1);
     load_step(st + 1);
     peek(st + 2);
-    if (st > 0) dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
+    dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
 
     // The two product stretches of the step run at raised wave priority: of
     // two waves of a SIMD in the same stretch, one then runs ahead and reaches
@@ -733,7 +772,9 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         const float lz = ri[t][e] * c_i - qls[e];     // log2 p_px
         const bool vis = u <= qcs[e];                  // -1 for rows that hold no query
         const float ez = __builtin_amdgcn_exp2f(vis ? lz : -INFINITY);
-        dz[t][e] = vis ? lam * (ez - pb[t][e]) : 0.f;
+        // No select: where the key is invisible to the query every head's
+        // P is 0 too (same cut), so pbar = 0, ez = 0 and dz = 0.
+        dz[t][e] = lam * (ez - pb[t][e]);
         if (EXTRA && dscore != nullptr && vis) {
           const int tq = tb[kQryT * 32 + r4 + e], sl = tb[kQrySlot * 32 + r4 + e];
           if ((unsigned)tq < (unsigned)N && (unsigned)sl < (unsigned)topk)
@@ -1006,9 +1047,9 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   prof_end(s);
-  // Index log-sum-exp over the selected support (items of <= 128 queries).
-  if ((e = launch_block_items(P, m, 0, P.N, kItemQueries, s)) != hipSuccess) return e;
-  size_t grid = block_items_upper_bound(P, 0, P.N, kItemQueries);
+  // Index log-sum-exp over the selected support (items of <= kLseItem queries).
+  if ((e = launch_block_items(P, m, 0, P.N, kLseItem, s)) != hipSuccess) return e;
+  size_t grid = block_items_upper_bound(P, 0, P.N, kLseItem);
   grid = (grid + 7) & ~size_t(7);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int n_lists = P.B * P.H_kv * P.nblk;
