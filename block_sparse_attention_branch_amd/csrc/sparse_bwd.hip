@@ -553,21 +553,12 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   };
   Pre pre;
   int pk_e = -1, pk_qi = -1, pk_qt = -1;
-  // List reads and atomics of a step are unconditional (clamped index, value
-  // selected afterwards), so the step has no branches the scheduler must
-  // respect and the latencies of its phases can overlap.
-  auto entry = [&](int qi) {
-    const int v = qlist[min(qi, kBlock + kBigItem - 1)];
-    return qi < nq ? v : -1;
-  };
+  auto entry = [&](int qi) { return qi < nq ? qlist[qi] : -1; };
   auto cutoff = [&](int qi, int t) { return t < 0 ? -1 : ((qi < it.n_own && causal) ? t : 0x7fffffff); };
   auto peek = [&](int st) {
-    const int e0 = entry(st * TQ + ld_rr / G);
-    const int e1 = entry(st * TQ + max(ld_qq, 0));
-    const int e2 = entry(st * TQ + max(mq_q, 0));
-    pk_e = ld_row ? e0 : -1;
-    pk_qi = (ld_qi && ld_qq >= 0) ? e1 : -1;
-    pk_qt = (tx < 32 && mq_q >= 0) ? e2 : -1;
+    pk_e = ld_row ? entry(st * TQ + ld_rr / G) : -1;
+    pk_qi = (ld_qi && ld_qq >= 0) ? entry(st * TQ + ld_qq) : -1;
+    pk_qt = (tx < 32 && mq_q >= 0) ? entry(st * TQ + mq_q) : -1;
   };
   // Unconditional loads (clamped to a valid row): the compiler counts them.
   auto load_step = [&](int st) {
@@ -651,11 +642,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (ri_query<G>(t, lq, e) >= 0) {
-          // A row without a query adds +0 to row 0 (dq_idx never holds -0,
-          // so no bit changes).
           const int id = tb[kQryId * 32 + 16 * t + 4 * lq + e];
-          const bool ok = (unsigned)id < (unsigned)n_grows;
-          atomicAdd(dq_idx + (size_t)(ok ? id : 0) * DIDX + 16 * ict + c, ok ? o[t][e] : 0.f);
+          if ((unsigned)id < (unsigned)n_grows) atomicAdd(dq_idx + (size_t)id * DIDX + 16 * ict + c, o[t][e]);
         }
   };
   // Store step st's dQ rows from its tile in LDS as bf16 partials (one row of
@@ -689,23 +677,16 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   load_step(0);
   store_step(0);
   peek(1);
-  // Step -1's row ids (tables of parity 1): none, so the first step's
-  // dq_idx and dQ stores of "step -1" add +0 to row 0 and write the spare
-  // partial row, and the loop needs no branch on st > 0.
-  if (tx < 32) {
-    tabs[NT + kRowId * 32 + tx] = -1;
-    tabs[NT + kQryId * 32 + tx] = -1;
-  }
 #pragma unroll 1
   for (int st = 0; st < n_steps; ++st) {
     asm volatile("" ::: "memory");
     const int* tb = tabs + (st & 1) * NT;
     const float* tf = reinterpret_cast<const float*>(tb);
     __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T / dz^T complete
-    dq_idx_step(st - 1);
+    if (st > 0) dq_idx_step(st - 1);
     load_step(st + 1);
     peek(st + 2);
-    dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
+    if (st > 0) dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
 
     // The two product stretches of the step run at raised wave priority: of
     // two waves of a SIMD in the same stretch, one then runs ahead and reaches
@@ -772,9 +753,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         const float lz = ri[t][e] * c_i - qls[e];     // log2 p_px
         const bool vis = u <= qcs[e];                  // -1 for rows that hold no query
         const float ez = __builtin_amdgcn_exp2f(vis ? lz : -INFINITY);
-        // No select: where the key is invisible to the query every head's
-        // P is 0 too (same cut), so pbar = 0, ez = 0 and dz = 0.
-        dz[t][e] = lam * (ez - pb[t][e]);
+        dz[t][e] = vis ? lam * (ez - pb[t][e]) : 0.f;
         if (EXTRA && dscore != nullptr && vis) {
           const int tq = tb[kQryT * 32 + r4 + e], sl = tb[kQrySlot * 32 + r4 + e];
           if ((unsigned)tq < (unsigned)N && (unsigned)sl < (unsigned)topk)

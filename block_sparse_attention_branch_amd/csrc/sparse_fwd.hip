@@ -139,46 +139,15 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
   // Stage K_j (row-major) and V_j^T in LDS.
   {
     const size_t base = (((size_t)b * N + (size_t)j * kBlock) * H_kv + g) * D;
-    if constexpr (C::EPC == 8 && D == 128) {
-      // bf16, d = 128: K rows as they are; V in 8 x 8 pieces (8 keys of one
-      // 8-column chunk per thread) transposed in registers, so that V^T goes
-      // to LDS as 8-byte runs of 4 keys instead of single elements.  Lanes
-      // 16 apart share a chunk column: a pass of 16 lanes writes 16 key runs
-      // of one V^T row pair, on distinct banks.
-      for (int c = threadIdx.x; c < kBlock * C::CPR; c += kFwdThreads) {
-        const int key = c / C::CPR, col = c % C::CPR;
-        *reinterpret_cast<uint4*>(Ks + key * C::PK + col * C::EPC) =
-            *reinterpret_cast<const uint4*>(k + base + (size_t)key * H_kv * D + col * C::EPC);
-      }
-      static_assert(kFwdThreads == 16 * (D / 8), "one 8 x 8 piece of V per thread");
-      const int k0 = 8 * (threadIdx.x % 16), col = threadIdx.x / 16;
-      bf16x8 r[8];
+    for (int c = threadIdx.x; c < kBlock * C::CPR; c += kFwdThreads) {
+      const int key = c / C::CPR, col = c % C::CPR;
+      const size_t goff = base + (size_t)key * H_kv * D + col * C::EPC;
+      const uint4 kv = *reinterpret_cast<const uint4*>(k + goff);
+      *reinterpret_cast<uint4*>(Ks + key * C::PK + col * C::EPC) = kv;
+      const uint4 vv = *reinterpret_cast<const uint4*>(v + goff);
+      const T* ve = reinterpret_cast<const T*>(&vv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        r[i] = *reinterpret_cast<const bf16x8*>(v + base + (size_t)(k0 + i) * H_kv * D + col * 8);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        bf16x4 lo, hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo[i] = r[i][dd];
-          hi[i] = r[4 + i][dd];
-        }
-        T* dst = Vt + (col * 8 + dd) * C::PV + k0;
-        *reinterpret_cast<bf16x4*>(dst) = lo;
-        *reinterpret_cast<bf16x4*>(dst + 4) = hi;
-      }
-    } else {
-      for (int c = threadIdx.x; c < kBlock * C::CPR; c += kFwdThreads) {
-        const int key = c / C::CPR, col = c % C::CPR;
-        const size_t goff = base + (size_t)key * H_kv * D + col * C::EPC;
-        const uint4 kv = *reinterpret_cast<const uint4*>(k + goff);
-        *reinterpret_cast<uint4*>(Ks + key * C::PK + col * C::EPC) = kv;
-        const uint4 vv = *reinterpret_cast<const uint4*>(v + goff);
-        const T* ve = reinterpret_cast<const T*>(&vv);
-#pragma unroll
-        for (int i = 0; i < C::EPC; ++i) Vt[(col * C::EPC + i) * C::PV + key] = ve[i];
-      }
+      for (int i = 0; i < C::EPC; ++i) Vt[(col * C::EPC + i) * C::PV + key] = ve[i];
     }
   }
   __syncthreads();
