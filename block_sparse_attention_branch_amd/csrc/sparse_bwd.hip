@@ -208,20 +208,39 @@ __global__ __launch_bounds__(256) void idx_lse_kernel(
 }
 
 // lse_idx (natural log) from the per-slot partials (log2-domain max, sum).
+// Four lanes per row, KM / 4 slots each (KM >= topk, a compile-time bound):
+// every load of the row is issued at once (slot indices past topk clamped to
+// the last slot and skipped), then a max and a sum over the four lanes.
+template <int KM>
 __global__ __launch_bounds__(256) void idx_lse_merge_kernel(const float2* __restrict__ part,
                                                             const int32_t* __restrict__ block_idx,
-                                                            float* __restrict__ lse_idx, size_t rows, int topk) {
-  const size_t r = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const int32_t* brow = block_idx + r * topk;
-  const float2* p = part + r * topk;
+                                                            float* __restrict__ lse_idx, int rows, int topk) {
+  constexpr int SPL = KM / 4;
+  const int r = (blockIdx.x * 256 + threadIdx.x) >> 2;
+  const int e0 = (threadIdx.x & 3) * SPL;
+  const bool live = r < rows;
+  const int rc = live ? r : rows - 1;
+  const int32_t* brow = block_idx + (size_t)rc * topk;
+  const float2* p = part + (size_t)rc * topk;
+  float2 pv[SPL];
+  bool ok[SPL];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int e = e0 + i, ec = min(e, topk - 1);
+    pv[i] = p[ec];
+    ok[i] = e < topk && brow[ec] >= 0;
+  }
   float m = -INFINITY;
-  for (int e = 0; e < topk; ++e)
-    if (brow[e] >= 0) m = fmaxf(m, p[e].x);
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) m = ok[i] ? fmaxf(m, pv[i].x) : m;
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));   // finite: the own block is always valid
   float l = 0.f;
-  for (int e = 0; e < topk; ++e)
-    if (brow[e] >= 0) l += p[e].y * exp2f(p[e].x - m);
-  lse_idx[r] = (m + log2f(l)) * kLn2;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) l += ok[i] ? pv[i].y * __builtin_amdgcn_exp2f(pv[i].x - m) : 0.f;
+  l += __shfl_xor(l, 1);
+  l += __shfl_xor(l, 2);
+  if (live && (threadIdx.x & 3) == 0) lse_idx[r] = (m + __builtin_amdgcn_logf(l)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1041,8 +1060,14 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
     hipLaunchKernelGGL(idx_lse_kernel<32>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16*>(a.q_idx),
                        static_cast<const bf16*>(a.k_idx), a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.idx_part,
                        P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, n_lists, P.scale_idx);
-  hipLaunchKernelGGL(idx_lse_merge_kernel, dim3((unsigned)((rows_g + 255) / 256)), dim3(256), 0, s, w.idx_part,
-                     a.block_idx, w.lse_idx, rows_g, P.topk);
+  {
+    if (rows_g > 0x1fffffff) return hipErrorInvalidConfiguration;
+    auto mk = P.topk <= 4 ? idx_lse_merge_kernel<4>
+            : P.topk <= 8 ? idx_lse_merge_kernel<8>
+            : P.topk <= 16 ? idx_lse_merge_kernel<16> : idx_lse_merge_kernel<32>;
+    hipLaunchKernelGGL(mk, dim3((unsigned)((rows_g * 4 + 255) / 256)), dim3(256), 0, s, w.idx_part, a.block_idx,
+                       w.lse_idx, (int)rows_g, P.topk);
+  }
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Main kernel per query chunk (long items: own queries + up to kBigItem
