@@ -45,6 +45,19 @@ struct IdxCfg {
   static constexpr size_t LDS_BYTES = 2 * TILE_ELEMS * sizeof(T);
 };
 
+// An empty asm that reads every 32-bit word of x: x must be in registers
+// (its loads complete) at this point of the program.
+template <typename F>
+__device__ inline void hold_in_registers(const F& x) {
+  static_assert(sizeof(F) % 4 == 0, "whole words");
+  struct Words {
+    unsigned w[sizeof(F) / 4];
+  };
+  const Words v = __builtin_bit_cast(Words, x);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(F) / 4); ++i) asm volatile("" ::"v"(v.w[i]));
+}
+
 template <typename T, int DIDX, int CAP>
 __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
@@ -95,26 +108,38 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
   }
 
   const char* kbase = reinterpret_cast<const char*>(k_idx + (size_t)b * N * DIDX);
-  uint4 stage[C::CHUNKS_PER_THREAD];
+  // A native 4 x 32-bit vector, not HIP's uint4 class: the class copy kept
+  // the staging array in scratch memory.
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 stage[C::CHUNKS_PER_THREAD];
   auto load_block = [&](int j) {
     const char* src = kbase + (size_t)j * kBlock * DIDX * sizeof(T);
 #pragma unroll
     for (int c = 0; c < C::CHUNKS_PER_THREAD; ++c) {
       const int chunk = threadIdx.x + c * kIdxThreads;
-      stage[c] = *reinterpret_cast<const uint4*>(src + (size_t)chunk * 16);
+      stage[c] = *reinterpret_cast<const u32x4*>(src + (size_t)chunk * 16);
     }
   };
+
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < C::CHUNKS_PER_THREAD; ++c) {
       const int chunk = threadIdx.x + c * kIdxThreads;
       const int row = chunk / C::CHUNKS_PER_ROW, col = chunk % C::CHUNKS_PER_ROW;
-      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds + buf * C::TILE_ELEMS + row * C::PITCH) +
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(lds + buf * C::TILE_ELEMS + row * C::PITCH) +
                                 col * 16) = stage[c];
     }
   };
 
   load_block(0);
+  // The query fragments are consumed here, before the loop, so their loads
+  // complete in the prologue: left in flight into the loop, the wait-count
+  // analysis merged them into the loop header and waited on every load in
+  // flight (the next block's included) before each block's first products.
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) hold_in_registers(qf[nt][ks]);
   store_block(0);
   __syncthreads();
 
@@ -139,6 +164,9 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
   for (int j = 0; j <= jlast; ++j) {
     const int buf = j & 1;
     const bool more = j < jlast;
+    // The next block is loaded here and goes to the other LDS buffer right
+    // after this block's products are issued, so its registers are not held
+    // (or re-loaded by the compiler) across the block's vector work.
     if (more) load_block(j + 1);
     const bool visible = wave_valid && (!causal || j <= own);
     const bool is_own = j == own;
@@ -158,6 +186,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
           a1[mt] = M::mma(a, qf[1][ks], a1[mt]);
         }
       }
+      if (more) store_block(buf ^ 1);
       if (j_prev >= 0) {
         insert(p_prev, j_prev);
         j_prev = -1;
@@ -189,8 +218,9 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
         p_prev = p;
         j_prev = j;
       }
+    } else if (more) {
+      store_block(buf ^ 1);
     }
-    if (more) store_block(buf ^ 1);
     __syncthreads();
   }
   if (j_prev >= 0) insert(p_prev, j_prev);

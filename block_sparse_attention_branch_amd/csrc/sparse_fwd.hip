@@ -15,7 +15,7 @@
 //
 // Structure (two kernels per query chunk):
 //   1. sparse_fwd_kernel: one workgroup per work item = (b, g, KV block j,
-//      up to 128 queries that selected j).  K_j and V_j^T are staged in LDS
+//      up to 384 queries that selected j, or its own 128).  K_j and V_j^T are staged in LDS
 //      once; each wave takes 32 (query, head) rows at a time:
 //        S^T = K_j Q^T      (32x32 MFMA: keys are tile rows, a lane holds
 //                            one (query, head) row and 16 keys per tile)
@@ -32,11 +32,17 @@
 namespace msa {
 namespace {
 
-constexpr int kFwdThreads = 256;      // 4 waves
-constexpr int kItemQueries = 256;     // list entries per work item (the diagonal item has its 128)
+
+constexpr int kItemQueries = 384;     // list entries per work item (the diagonal item has its 128)
 
 template <typename T, int D>
 struct FwdCfg {
+  // bf16: 12 waves, one workgroup per CU (99 KB of LDS at d = 128), three
+  // waves per SIMD (at most 168 VGPRs each), so that a SIMD has a third wave
+  // to issue from while two wait.  fp32 tiles take twice the LDS: 4 waves,
+  // two workgroups per CU at d = 64, one at d = 128.
+  static constexpr int WAVES = sizeof(T) == 2 ? 12 : 4;
+  static constexpr int THREADS = 64 * WAVES;
   static constexpr int KPL = Mma<T>::KPL;
   static constexpr int KSTEPS = D / (2 * KPL);           // k-steps of S^T over d
   static constexpr int KCH = 16 / KPL;                   // B-operand chunks per 32-key tile
@@ -47,7 +53,7 @@ struct FwdCfg {
   // Per-wave staging of one 32-column slice of the partial output (32 rows),
   // so that the partials leave in 16-byte pieces, 64 bytes per row per slice.
   static constexpr int PO = 32 + 16 / (int)sizeof(T);                  // row pitch (elements)
-  static constexpr size_t O_BYTES = (size_t)(kFwdThreads / 64) * 32 * PO * sizeof(T);
+  static constexpr size_t O_BYTES = (size_t)WAVES * 32 * PO * sizeof(T);
   static constexpr size_t LDS = K_BYTES + V_BYTES + O_BYTES;
   static constexpr int DT = D / 32;
   static constexpr int CPR = D * (int)sizeof(T) / 16;    // 16-byte chunks per key row
@@ -99,7 +105,7 @@ template <> struct Store4<float> {
 };
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
+__global__ __launch_bounds__((FwdCfg<T, D>::THREADS), (FwdCfg<T, D>::WAVES / 4)) void sparse_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ rows, const int32_t* __restrict__ tiles,
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
   // Stage K_j (row-major) and V_j^T in LDS.
   {
     const size_t base = (((size_t)b * N + (size_t)j * kBlock) * H_kv + g) * D;
-    for (int c = threadIdx.x; c < kBlock * C::CPR; c += kFwdThreads) {
+    for (int c = threadIdx.x; c < kBlock * C::CPR; c += C::THREADS) {
       const int key = c / C::CPR, col = c % C::CPR;
       const size_t goff = base + (size_t)key * H_kv * D + col * C::EPC;
       const uint4 kv = *reinterpret_cast<const uint4*>(k + goff);
@@ -155,21 +161,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_rows = nq * G;
   const float c_exp = scale * kLog2e;
-  // The list entries of this lane's row in each of the wave's row tiles (at
-  // most kItemQueries * G / 128 of them), read up front so that no row tile
-  // waits for an entry before it can load its queries.
-  constexpr int kTiles = kItemQueries * G / 128;
-  int ents[kTiles];
-  if (!diag) {
-#pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      const int r = wave * 32 + i * 128 + (lane & 31);
-      ents[i] = r < n_rows ? ent[r / G] : 0;
-    }
-  }
+  constexpr int NW = C::WAVES;
   // Query, slot and validity of this lane's row in the wave's row tile
-  // `tile` (rows r0 = 32 wave + 128 tile ..).
-  auto locate = [&](int r0, int tile, int* t, int* slot, int* h, bool* valid) {
+  // starting at row r0 (rows r0 = 32 wave + 32 WAVES tile ..).
+  auto locate = [&](int r0, int* t, int* slot, int* h, bool* valid) {
     const int r = r0 + (lane & 31);
     const int qi = r / G;
     *h = g * G + r % G;
@@ -181,10 +176,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
       for (int e = 0; e < topk; ++e)
         if (brow[e] == j) *slot = e;
     } else {
-      int e = ents[0];
-#pragma unroll
-      for (int i = 1; i < kTiles; ++i)
-        if (tile == i) e = ents[i];
+      // The list entry is read here, one row tile ahead of its use (the
+      // next tile is located while the current one computes).
+      const int e = ent[min(r, n_rows - 1) / G];
       *t = e >> 6;
       *slot = e & 63;
       // A well-formed map only yields queries of this chunk; anything else is
@@ -204,10 +198,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
   };
   int nt, nslot, nh;
   bool nvalid;
-  locate(wave * 32, 0, &nt, &nslot, &nh, &nvalid);
+  locate(wave * 32, &nt, &nslot, &nh, &nvalid);
   if (wave * 32 < n_rows) load_q(nt, nh);
 #pragma unroll 1
-  for (int r0 = wave * 32, tile = 0; r0 < n_rows; r0 += 128, ++tile) {
+  for (int r0 = wave * 32; r0 < n_rows; r0 += 32 * NW) {
     // Keep the K/V fragment reads inside the loop (re-read from LDS per row
     // tile) instead of letting them be hoisted into ~256 live registers.
     asm volatile("" ::: "memory");
@@ -217,7 +211,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = qn[ks];
 
+    // The S and O product stretches run at raised wave priority, so that of
+    // two waves of a SIMD the one issuing products goes first and the other's
+    // softmax fills the vector unit meanwhile.
     f32x16 s[4];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       s[mt] = zero16();
@@ -225,6 +223,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks) s[mt] = M::mma(M::load(kp + ks * 2 * KPL), qf[ks], s[mt]);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (diag && causal) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -244,7 +243,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const float p = exp2f(s[mt][vv] * c_exp - mc);
+        // The hardware exp2 (one instruction; its argument is <= 0 here, and
+        // results below the fp32 normal range are negligible beside the
+        // row's maximum of 1), not the library's range-reduced exp2f.
+        const float p = __builtin_amdgcn_exp2f(s[mt][vv] * c_exp - mc);
         s[mt][vv] = p;
         lsum += p;
       }
@@ -252,8 +254,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
 
     // The next row tile's queries: located and their Q loads issued here, so
     // that the O products and partial stores of this tile cover the gather.
-    if (r0 + 128 < n_rows) {
-      locate(r0 + 128, tile + 1, &nt, &nslot, &nh, &nvalid);
+    if (r0 + 32 * NW < n_rows) {
+      locate(r0 + 32 * NW, &nt, &nslot, &nh, &nvalid);
       load_q(nt, nh);
     }
 
@@ -265,6 +267,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
       for (int kc = 0; kc < C::KCH; ++kc) pf[mt][kc] = VtFrag<T>::pfrag(s[mt], kc);
 
     f32x16 o[C::DT];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       o[dt] = zero16();
@@ -276,6 +279,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void sparse_fwd_kernel(
           o[dt] = M::mma(a, pf[mt][kc], o[dt]);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // Partial o of the row (normalised) and its LSE.  Each 32-column slice
     // goes through the wave's LDS staging tile: lane (row, half) writes its
@@ -438,7 +442,7 @@ hipError_t run_fwd(const Problem& P, const T* q, const T* k, const T* v, const i
     const int s_lo = c0 / span;
     const int s_hi = (c1 == P.N) ? m.nsb : c1 / span;
     prof_begin("fwd_partial", s);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kFwdThreads), C::LDS, s, q, k, v, block_idx, m.pos,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS, s, q, k, v, block_idx, m.pos,
                        m.offs, m.rows, m.tiles, po, pl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, s_lo,
                        s_hi, c0, c1, n_lists, P.scale);
     prof_end(s);
