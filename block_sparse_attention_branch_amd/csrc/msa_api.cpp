@@ -60,6 +60,9 @@ int check_dims(const msa_dims* d, msa::Problem* P) {
   if (d->N % msa::kBlock != 0)
     return fail(MSA_ERR_UNSUPPORTED, "N=%d is not a multiple of the block size %d", d->N, msa::kBlock);
   if (d->N > kMaxN) return fail(MSA_ERR_UNSUPPORTED, "N=%d exceeds %d", d->N, kMaxN);
+  // Query-row indices (b, t, head) are 32-bit inside the kernels.
+  if ((long long)d->B * d->N * d->H_q > 0x7fffffffLL)
+    return fail(MSA_ERR_UNSUPPORTED, "B*N*H_q=%lld rows exceed 2^31-1", (long long)d->B * d->N * d->H_q);
   if (d->d != 64 && d->d != 128) return fail(MSA_ERR_UNSUPPORTED, "head dim d=%d (64 or 128)", d->d);
   if (d->d_idx != 32 && d->d_idx != 64)
     return fail(MSA_ERR_UNSUPPORTED, "index dim d_idx=%d (32 or 64)", d->d_idx);

@@ -580,32 +580,42 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     pk_qt = (tx < 32 && mq_q >= 0) ? entry(st * TQ + mq_q) : -1;
   };
   // Unconditional loads (clamped to a valid row): the compiler counts them.
+  // Row indices are 32-bit (B N H_q < 2^31, checked by the host), with the
+  // thread's constant column and head folded into base pointers, so a step's
+  // addresses cost a 32-bit multiply-add and a shift each.
+  const int hq_ld = g * G + ld_rr % G;                       // head of the thread's Q / dO row
+  const int bN = b * N;
+  const bf16* q_ld = q + (size_t)hq_ld * D + ld_col;
+  const bf16* dO_ld = dO + (size_t)hq_ld * D + ld_col;
+  const float* lse_ld = lse + hq_ld;
+  const float* Dv_ld = Dv + hq_ld;
+  const bf16* qi_ld = q_idx + (size_t)g * DIDX + ld_qcol;
+  const int id_base = b * CQ - c0;                            // chunk-local query of t: id_base + t
   auto load_step = [&](int st) {
     {
       const int t = pk_e < 0 ? -1 : (pk_e >> 6);
       pre.t = t;
       pre.cut = cutoff(st * TQ + ld_rr / G, t);
-      const size_t qrow = ((size_t)b * N + (t < 0 ? 0 : t)) * H_q + g * G + ld_rr % G;
+      const int qrow = (bN + max(t, 0)) * H_q;                // row of (b, t, head 0)
       // dQ partial row of (t, head, slot) within the query chunk.
       const bool in_chunk = t >= c0 && t < c0 + CQ;
-      pre.id = in_chunk ? (((b * CQ + (t - c0)) * topk + (pk_e & 63)) * H_q + g * G + ld_rr % G) : -1;
-      pre.q = *reinterpret_cast<const bf16x8*>(q + qrow * D + ld_col);
-      pre.d = *reinterpret_cast<const bf16x8*>(dO + qrow * D + ld_col);
-      pre.lse = lse[qrow];
-      pre.rd = Dv[qrow];
+      pre.id = in_chunk ? (((id_base + t) * topk + (pk_e & 63)) * H_q + hq_ld) : -1;
+      pre.q = *reinterpret_cast<const bf16x8*>(q_ld + (size_t)qrow * D);
+      pre.d = *reinterpret_cast<const bf16x8*>(dO_ld + (size_t)qrow * D);
+      pre.lse = lse_ld[qrow];
+      pre.rd = Dv_ld[qrow];
     }
     {
       const int tq = pk_qi < 0 ? -1 : (pk_qi >> 6);
-      pre.qi = *reinterpret_cast<const bf16x8*>(q_idx + (((size_t)b * N + (tq < 0 ? 0 : tq)) * H_kv + g) * DIDX +
-                                                ld_qcol);
+      pre.qi = *reinterpret_cast<const bf16x8*>(qi_ld + (size_t)((bN + max(tq, 0)) * H_kv) * DIDX);
       if (tq < 0) pre.qi = bf16x8{};
     }
     {
       pre.qt = pk_qt < 0 ? -1 : (pk_qt >> 6);
       pre.qslot = pk_qt < 0 ? 0 : (pk_qt & 63);
       pre.qcut = cutoff(st * TQ + (mq_q < 0 ? 0 : mq_q), pre.qt);
-      const size_t qrow = ((size_t)b * N + (pre.qt < 0 ? 0 : pre.qt)) * H_kv + g;
-      pre.qid = pre.qt < 0 ? -1 : (int)qrow;
+      const int qrow = (bN + max(pre.qt, 0)) * H_kv + g;
+      pre.qid = pre.qt < 0 ? -1 : qrow;
       pre.qlse = lse_idx[qrow];
     }
   };
@@ -676,13 +686,14 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     const int row = 4 * wave + (lane / LPR) % 4;
     const int col = (lane % LPR) * 8;
     if (lane < 4 * LPR) {
-      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float x[8];
 #pragma unroll
       for (int kp = 0; kp < C::KPQ; ++kp) {
         const float4 a0 = *reinterpret_cast<const float4*>(dQt + (kp * 32 + row) * C::PDQ + col);
         const float4 a1 = *reinterpret_cast<const float4*>(dQt + (kp * 32 + row) * C::PDQ + col + 4);
-        x[0] += a0.x; x[1] += a0.y; x[2] += a0.z; x[3] += a0.w;
-        x[4] += a1.x; x[5] += a1.y; x[6] += a1.z; x[7] += a1.w;
+        const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = kp == 0 ? a[i] : x[i] + a[i];   // no 0 + a for the first part
       }
       bf16x8 y;
 #pragma unroll
@@ -812,19 +823,29 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     // at the top of the next step, whose barrier completes it.  Nothing reads
     // the tile between the barrier above and this write.
     {
+      // The K operands are read once for both row tiles, and the tile is
+      // written after all products (an LDS write between them would make the
+      // compiler read K again for the second tile).
+      bf16x8 kq[4 / KPQ];
+#pragma unroll
+      for (int ks = 0; ks < 4 / KPQ; ++ks) {
+        const int k0 = 32 * (qkp * (4 / KPQ) + ks) + 4 * lq;   // keys k0 .. k0+3, k0+16 .. k0+19
+        kq[ks] = tr16<typename C::TK>(Ks, 16 * qct, k0, k0 + 16, lane);
+      }
       f32x4 o[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         o[t] = zero4();
 #pragma unroll
         for (int ks = 0; ks < 4 / KPQ; ++ks) {
-          const int k0 = 32 * (qkp * (4 / KPQ) + ks) + 4 * lq;   // keys k0 .. k0+3, k0+16 .. k0+19
-          o[t] = mma16(tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane),
-                       tr16<typename C::TK>(Ks, 16 * qct, k0, k0 + 16, lane), o[t]);
+          const int k0 = 32 * (qkp * (4 / KPQ) + ks) + 4 * lq;
+          o[t] = mma16(tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane), kq[ks], o[t]);
         }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) dQt[(qkp * 32 + 16 * t + 4 * lq + e) * C::PDQ + 16 * qct + c] = o[t][e];
-      }
     }
     if (EXTRA && kl != nullptr && threadIdx.x < 32) {
       const int id = tb[kQryId * 32 + threadIdx.x];

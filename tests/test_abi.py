@@ -71,6 +71,7 @@ def good_dims(**kw):
     (dict(topk=33), bnd.MSA_ERR_UNSUPPORTED),
     (dict(H_q=6, H_kv=2), bnd.MSA_ERR_UNSUPPORTED),
     (dict(N=128 * (1 << 16)), bnd.MSA_ERR_UNSUPPORTED),
+    (dict(B=128, N=1 << 20, H_q=16, H_kv=2), bnd.MSA_ERR_UNSUPPORTED),   # B*N*H_q = 2^31
 ])
 def test_invalid_dims_rejected_by_every_entry_point(lib, kw, expect):
     dims = good_dims(**kw)
