@@ -108,9 +108,8 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
   }
 
   const char* kbase = reinterpret_cast<const char*>(k_idx + (size_t)b * N * DIDX);
-  // A native 4 x 32-bit vector, not HIP's uint4 class: the class copy kept
+  // Native 4 x 32-bit vectors, not HIP's uint4 class: the class copy kept
   // the staging array in scratch memory.
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   u32x4 stage[C::CHUNKS_PER_THREAD];
   auto load_block = [&](int j) {
     const char* src = kbase + (size_t)j * kBlock * DIDX * sizeof(T);

@@ -46,6 +46,8 @@ struct fp8e4m3 {
   uint8_t bits;
 };
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+// Native 4 x 32-bit vector (the type the nontemporal builtins take).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // gfx950 FP8 matrix unit, 32x32x64 per instruction: lane l holds 32
 // consecutive k values of row (A) or column (B) l % 32, the half of k chosen
 // by l / 32, as for the other 32x32 forms; both operands E4M3 (format code 0)

@@ -700,7 +700,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
       for (int i = 0; i < 8; ++i) y[i] = (bf16)x[i];
       const int id = tb[kRowId * 32 + row];
       const int dst = (unsigned)id < (unsigned)n_prow ? id : n_prow;
-      *reinterpret_cast<bf16x8*>(dq_part + (size_t)dst * D + col) = y;
+      // Streaming store: the partials are read once, by dq_merge_kernel.
+      __builtin_nontemporal_store(y, reinterpret_cast<bf16x8*>(dq_part + (size_t)dst * D + col));
     }
   };
   peek(0);
@@ -903,7 +904,8 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(const bf16* __restrict__ 
   const bf16* prow = part + ((size_t)bt * topk * H_q + h) * D + col;   // slot e at + e H_q D
   bf16x8 raw[KM];
 #pragma unroll
-  for (int e = 0; e < KM; ++e) raw[e] = *reinterpret_cast<const bf16x8*>(prow + (size_t)min(e, topk - 1) * H_q * D);
+  for (int e = 0; e < KM; ++e)   // streaming loads: each partial is read once
+    raw[e] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(prow + (size_t)min(e, topk - 1) * H_q * D));
   bool ok[KM];
   if (topk == KM) {
 #pragma unroll

@@ -311,7 +311,12 @@ __global__ __launch_bounds__((FwdCfg<T, D>::THREADS), (FwdCfg<T, D>::WAVES / 4))
           const int rr = i * RPI + lane / PPR, pc = lane % PPR;
           const int sb = __shfl(sbase, rr);
           const uint4 x = *reinterpret_cast<const uint4*>(ost + rr * C::PO + pc * EPC);
-          if (sb >= 0) *reinterpret_cast<uint4*>(po + (size_t)(sb + dt * H_q) * 32 + pc * EPC) = x;
+          // Streaming (nontemporal) store: the partials are read once, by the
+          // merge, so they should not displace the Q rows and K/V blocks
+          // that the other items re-read from the caches.
+          if (sb >= 0)
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x),
+                                        reinterpret_cast<u32x4*>(po + (size_t)(sb + dt * H_q) * 32 + pc * EPC));
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slice read before it is overwritten
       }
@@ -353,7 +358,8 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po
   uint4 raw[KM];
 #pragma unroll
   for (int e = 0; e < KM; ++e)
-    raw[e] = *reinterpret_cast<const uint4*>(prow + (size_t)min(e, topk - 1) * NS * H_q * 32);
+    raw[e] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                           prow + (size_t)min(e, topk - 1) * NS * H_q * 32)));   // read once
   // Slot log-sum-exps in log2 units, -inf for padded slots.
   float lv[KM];
   if (topk == KM) {
