@@ -93,11 +93,15 @@ COPY_SYMBOL = "neg_kernel"
 
 
 def source_sha(kernel: str) -> str | None:
+    """sha256 over the kernel's source file and the shared device header it
+    includes (work-item mapping, MFMA helpers)."""
     f = KERNEL_SOURCE.get(kernel)
     if f is None:
         return None
-    path = os.path.join(ROOT, "block_sparse_attention_branch_amd", "csrc", f)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for name in (f, "msa_internal.h"):
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_branch_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel: str, workload: str):

@@ -25,8 +25,8 @@
 //      and writes the normalised partial o_j (dtype) and its log-sum-exp.
 //   2. fwd_merge_kernel: per (query, head), LSE = logsumexp over its slots
 //      and o = sum_j exp(lse_j - LSE) o_j.
-//   The workgroup -> item map keeps consecutive items (same KV block) on one
-//   XCD, so a block's K/V stay in that XCD's L2 across its items.
+//   Item i is workgroup i, so consecutive items (same KV block) are dealt to
+//   different XCDs and the uneven item costs spread evenly over the chip.
 #include "msa_internal.h"
 
 namespace msa {
