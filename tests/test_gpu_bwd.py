@@ -77,6 +77,15 @@ def test_bwd_topk_edges(topk):
     _full(w)
 
 
+@pytest.mark.parametrize("B,N", [(3, 128), (2, 1152)])
+def test_bwd_single_block_and_ragged(B, N):
+    # N = 128: every row's support is its own causal prefix and p_px, pbar
+    # live on the one block; N = 1152: partial last items and index tiles.
+    w = msa_inputs.Workload(f"bwd-ragged-{N}", B=B, N=N, H_q=8, H_kv=2, d=128, d_idx=64, topk=16,
+                            backward=True, seed=250 + N)
+    _full(w)
+
+
 def test_bwd_kl_weight_scales_index_gradients():
     w = msa_inputs.Workload("bwd-lam", B=1, N=1024, H_q=16, H_kv=2, d=128, d_idx=64, topk=4, backward=True, seed=230)
     _full(w, lam=0.37)

@@ -81,6 +81,14 @@ def test_bf16_forward_topk_edges():
         _check_full(w)
 
 
+@pytest.mark.parametrize("B,N", [(3, 128), (2, 1152)])
+def test_bf16_forward_single_block_and_ragged(B, N):
+    # N = 128: one block, the own block, under the causal mask, every other
+    # slot padding.  N = 1152: the last index tile and work items are partial.
+    w = msa_inputs.Workload(f"bf16-ragged-{N}", B=B, N=N, H_q=8, H_kv=2, d=128, d_idx=64, topk=16, seed=91 + N)
+    _check_full(w)
+
+
 def test_zero_query_closed_form():
     """q = 0: every score is 0, so O is the mean of V over S(t) and the LSE
     is ln |S(t)| - for every row, which pins the mask and the support."""

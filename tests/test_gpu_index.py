@@ -105,6 +105,19 @@ def test_topk_larger_than_blocks_pads():
         assert s[t].tolist() == list(range(own + 1)) + [-1] * (8 - own - 1)
 
 
+@pytest.mark.parametrize("B,N,H_kv", [(3, 128, 2), (2, 1152, 2), (1, 640, 1)])
+def test_bf16_integer_ragged_query_tiles(B, N, H_kv):
+    # A workgroup covers 64 queries per wave (256 at H_kv = 2, 512 at H_kv = 1):
+    # these lengths leave whole waves past the end of the sequence, and N = 128
+    # is the one-block sequence whose rows hold the own block and padding only.
+    w = msa_inputs.Workload(f"bf16-int-ragged-{N}", B=B, N=N, H_q=2 * H_kv, H_kv=H_kv, d=64, d_idx=64, topk=4,
+                            seed=43 + N)
+    _check_full(w, "int", exact=True)
+    if N == 128:
+        sel = _run(w, "int", True, True, False)[1][0].cpu().numpy()
+        assert (sel[..., 0] == 0).all() and (sel[..., 1:] == -1).all()
+
+
 def test_bf16_integer_h_kv_odd_groups():
     # H_kv = 3 (groups per workgroup fall back to 1) and a non-causal pass.
     w = msa_inputs.Workload("bf16-int-hkv3", B=1, N=1536, H_q=6, H_kv=3, d=64, d_idx=64, topk=4, seed=41)
