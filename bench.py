@@ -369,7 +369,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+        print(f"bench.py measures one GPU: libmsa has no multi-GPU path (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}); run it with --gpus 1.", file=sys.stderr)
         return 2
 
