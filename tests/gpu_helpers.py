@@ -100,18 +100,22 @@ def _super_span(w: msa_inputs.Workload) -> int:
     return sb * w.block_size
 
 
-def _chunk(w: msa_inputs.Workload, per_q: int) -> int:
+def _chunk(w: msa_inputs.Workload, per_q: int, q_cap: int | None = None) -> int:
     span = _super_span(w)
     q = (40 << 30) // per_q
+    if q_cap is not None:
+        q = min(q, q_cap)
     q -= q % span
     return max(span, min(q, w.N))
 
 
 def fwd_chunk_queries(w: msa_inputs.Workload) -> int:
     """Queries per forward launch, as the library plans it (for sampling rows
-    at chunk seams): partials of at most 40 GiB."""
+    at chunk seams): partials of at most 40 GiB, and at most 128 MiB of q rows
+    per (batch, group) slice of the chunk."""
     esz = 2 if w.dtype == "bf16" else 4
-    return _chunk(w, w.B * w.H_q * w.topk * (w.d * esz + 4))
+    G = w.H_q // w.H_kv
+    return _chunk(w, w.B * w.H_q * w.topk * (w.d * esz + 4), (128 << 20) // (G * w.d * esz))
 
 
 def bwd_chunk_queries(w: msa_inputs.Workload) -> int:
