@@ -128,6 +128,39 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _shapes(spec, **tensors):
+    """Check every tensor against its expected shape before anything reaches
+    the library: the kernels index each buffer with sizes taken from the
+    others, so a mismatch would read or write past an allocation.
+
+    spec: {name: tuple of dimension names or ints}; the first tensor to name
+    a dimension fixes its size.  All tensors must also share one device."""
+    sizes = {}
+    device = None
+    for name, want in spec.items():
+        t = tensors[name]
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != len(want):
+            raise ValueError(f"{name} must have {len(want)} dimensions {tuple(want)}, got shape {tuple(t.shape)}")
+        for axis, (dim, n) in enumerate(zip(want, t.shape)):
+            if isinstance(dim, int):
+                ok = n == dim
+                expect = dim
+            else:
+                expect = sizes.setdefault(dim, n)
+                ok = n == expect
+            if not ok:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}: axis {axis} ({dim}) must be {expect}")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+    return sizes
+
+
 def _workspace(nbytes: int, device):
     if nbytes == 0:
         return None
@@ -138,9 +171,10 @@ def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int = 16, block_s
                causal: bool = True, return_pooled: bool = False):
     """block_idx [B,N,H_kv,topk] int32 (and pooled [B,N,H_kv,N/block_size] fp32).
     q_idx, k_idx: bf16, fp32, or float8_e4m3fn (d_idx = 64) for the FP8 indexer."""
-    lib = load_library()
+    _shapes({"q_idx": ("B", "N", "H_kv", "d_idx"), "k_idx": ("B", "N", "d_idx")}, q_idx=q_idx, k_idx=k_idx)
     _need(q_idx, "q_idx")
     _need(k_idx, "k_idx", q_idx.dtype)
+    lib = load_library()
     B, N, H_kv, d_idx = q_idx.shape
     dims = make_dims(B, N, H_kv, H_kv, 64, d_idx, block_size, topk, causal, _dtype_code(q_idx))
     out = torch.empty((B, N, H_kv, topk), dtype=torch.int32, device=q_idx.device)
@@ -158,10 +192,12 @@ def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int = 16, block_s
 def sparse_fwd(q, k, v, block_idx, d_idx: int = 64, block_size: int = 128, causal: bool = True,
                scale: float | None = None):
     """o [B,N,H_q,d] (dtype of q) and lse [B,N,H_q] fp32."""
-    lib = load_library()
+    _shapes({"q": ("B", "N", "H_q", "d"), "k": ("B", "N", "H_kv", "d"), "v": ("B", "N", "H_kv", "d"),
+             "block_idx": ("B", "N", "H_kv", "topk")}, q=q, k=k, v=v, block_idx=block_idx)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype)
     _need(block_idx, "block_idx", torch.int32)
+    lib = load_library()
     B, N, H_q, d = q.shape
     H_kv = k.shape[2]
     topk = block_idx.shape[3]
@@ -181,11 +217,16 @@ def sparse_bwd(q, k, v, o, dO, lse, block_idx, q_idx, k_idx, kl_weight: float = 
                scale_idx: float | None = None, want_dscore: bool = False, want_kl: bool = False):
     """dict with dq, dk, dv (dtype of q), dq_idx, dk_idx (fp32) and optionally
     dscore [B,N,H_kv,topk,block_size] and kl [B,N,H_kv] (fp32)."""
-    lib = load_library()
+    _shapes({"q": ("B", "N", "H_q", "d"), "k": ("B", "N", "H_kv", "d"), "v": ("B", "N", "H_kv", "d"),
+             "o": ("B", "N", "H_q", "d"), "dO": ("B", "N", "H_q", "d"), "lse": ("B", "N", "H_q"),
+             "block_idx": ("B", "N", "H_kv", "topk"), "q_idx": ("B", "N", "H_kv", "d_idx"),
+             "k_idx": ("B", "N", "d_idx")},
+            q=q, k=k, v=v, o=o, dO=dO, lse=lse, block_idx=block_idx, q_idx=q_idx, k_idx=k_idx)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"), (q_idx, "q_idx"), (k_idx, "k_idx")):
         _need(t, n, q.dtype)
     _need(lse, "lse", torch.float32)
     _need(block_idx, "block_idx", torch.int32)
+    lib = load_library()
     B, N, H_q, d = q.shape
     H_kv = k.shape[2]
     d_idx = q_idx.shape[3]

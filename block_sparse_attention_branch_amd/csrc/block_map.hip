@@ -196,7 +196,7 @@ hipError_t launch_block_map(const Problem& P, const int32_t* block_idx, const Bl
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  prof_begin("block_map", s);
+  ProfScope prof("block_map", s);
   hipLaunchKernelGGL(bm_count_kernel, dim3(n_bg * m.nsb), dim3(256), lds, s, block_idx, m.pos, P.N,
                      P.H_kv, P.topk, P.nblk, m.nsb, m.SB);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -211,7 +211,6 @@ hipError_t launch_block_map(const Problem& P, const int32_t* block_idx, const Bl
                        m.rows, P.N, P.H_kv, P.topk, P.nblk, m.nsb, m.SB);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  prof_end(s);
   return hipSuccess;
 }
 
@@ -269,10 +268,9 @@ hipError_t launch_block_items(const Problem& P, const BlockMap& m, int q_lo, int
   const int n_bg = P.B * P.H_kv;
   const int s_lo = q_lo / (m.SB * kBlock);
   const int s_hi = (q_hi == P.N) ? m.nsb : q_hi / (m.SB * kBlock);
-  prof_begin("block_items", s);
+  ProfScope prof("block_items", s);
   hipLaunchKernelGGL(bm_items_kernel, dim3(1), dim3(1024), 0, s, m.pos, m.tiles, P.nblk, m.nsb, n_bg, s_lo,
                      s_hi, q_lo / kBlock, (q_hi + kBlock - 1) / kBlock, item_queries, merge_diag);
-  prof_end(s);
   return hipGetLastError();
 }
 

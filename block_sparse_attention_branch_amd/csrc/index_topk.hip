@@ -264,11 +264,10 @@ hipError_t launch_typed(const Problem& P, const void* q_idx, const void* k_idx, 
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  prof_begin("index_topk", s);
+  ProfScope prof("index_topk", s);
   hipLaunchKernelGGL(kern, grid, dim3(kIdxThreads), C::LDS_BYTES, s, static_cast<const T*>(q_idx),
                      static_cast<const T*>(k_idx), block_idx, pooled, P.N, P.H_kv, P.topk, P.causal,
                      GT, n_qtiles, n_gtiles);
-  prof_end(s);
   return hipGetLastError();
 }
 

@@ -125,6 +125,16 @@ hipError_t launch_fill_f32(float* p, size_t n, float value, hipStream_t s);
 // the same thread and stream.
 void prof_begin(const char* name, hipStream_t s);
 void prof_end(hipStream_t s);
+// One timed region: prof_begin on construction, prof_end on every way out of
+// the scope (early error returns included), so a recorded start event is
+// never left pending.
+struct ProfScope {
+  hipStream_t s;
+  ProfScope(const char* name, hipStream_t st) : s(st) { prof_begin(name, st); }
+  ~ProfScope() { prof_end(s); }
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+};
 
 hipError_t launch_index_topk(const Problem& P, const void* q_idx, const void* k_idx,
                              int32_t* block_idx, float* pooled, hipStream_t s);

@@ -1048,7 +1048,8 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
   const size_t rows_q = (size_t)P.B * P.N * P.H_q;
   const size_t rows_g = (size_t)P.B * P.N * P.H_kv;
   // Zero every accumulator (fill kernels: safe inside captured graphs).
-  prof_begin("bwd_prep", s);
+  {
+  ProfScope prof("bwd_prep", s);
   if ((e = launch_fill_f32(w.dk_acc, rows_g * P.d, 0.f, s)) != hipSuccess) return e;
   if ((e = launch_fill_f32(w.dv_acc, rows_g * P.d, 0.f, s)) != hipSuccess) return e;
   if ((e = launch_fill_f32(a.dq_idx, rows_g * P.d_idx, 0.f, s)) != hipSuccess) return e;
@@ -1067,14 +1068,15 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
                          static_cast<const bf16*>(a.dO), static_cast<const bf16*>(a.o), w.D, rows_q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  prof_end(s);
+  }
   // Index log-sum-exp over the selected support (items of <= kLseItem queries).
   if ((e = launch_block_items(P, m, 0, P.N, kLseItem, s)) != hipSuccess) return e;
   size_t grid = block_items_upper_bound(P, 0, P.N, kLseItem);
   grid = (grid + 7) & ~size_t(7);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int n_lists = P.B * P.H_kv * P.nblk;
-  prof_begin("bwd_idx_lse", s);
+  {
+  ProfScope prof("bwd_idx_lse", s);
   if (P.d_idx == 64)
     hipLaunchKernelGGL(idx_lse_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16*>(a.q_idx),
                        static_cast<const bf16*>(a.k_idx), a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.idx_part,
@@ -1091,8 +1093,8 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
     hipLaunchKernelGGL(mk, dim3((unsigned)((rows_g * 4 + 255) / 256)), dim3(256), 0, s, w.idx_part, a.block_idx,
                        w.lse_idx, (int)rows_g, P.topk);
   }
-  prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // Main kernel per query chunk (long items: own queries + up to kBigItem
   // list entries), then the chunk's dq from its partials.
   const int chunk = bwd_chunk_queries(P);
@@ -1106,25 +1108,25 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
     if (g2 > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int s_lo = c0 / span;
     const int s_hi = (c1 == P.N) ? m.nsb : c1 / span;
-    prof_begin("bwd_main", s);
-    if (P.d == 128 && P.d_idx == 64) e = run_main_g<128, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
-    else if (P.d == 128) e = run_main_g<128, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
-    else if (P.d_idx == 64) e = run_main_g<64, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
-    else e = run_main_g<64, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
-    prof_end(s);
-    if (e != hipSuccess) return e;
-    prof_begin("bwd_dq_merge", s);
-    e = P.d == 128 ? launch_dq_merge<128>(P, w.dq_part, a.block_idx, static_cast<bf16*>(a.dq), c0, CQ, s)
-                   : launch_dq_merge<64>(P, w.dq_part, a.block_idx, static_cast<bf16*>(a.dq), c0, CQ, s);
-    prof_end(s);
-    if (e != hipSuccess) return e;
+    {
+      ProfScope prof("bwd_main", s);
+      if (P.d == 128 && P.d_idx == 64) e = run_main_g<128, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+      else if (P.d == 128) e = run_main_g<128, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+      else if (P.d_idx == 64) e = run_main_g<64, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+      else e = run_main_g<64, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+      if (e != hipSuccess) return e;
+    }
+    {
+      ProfScope prof("bwd_dq_merge", s);
+      e = P.d == 128 ? launch_dq_merge<128>(P, w.dq_part, a.block_idx, static_cast<bf16*>(a.dq), c0, CQ, s)
+                     : launch_dq_merge<64>(P, w.dq_part, a.block_idx, static_cast<bf16*>(a.dq), c0, CQ, s);
+      if (e != hipSuccess) return e;
+    }
   }
   // fp32 accumulators to bf16 outputs.
-  prof_begin("bwd_finalize", s);
+  ProfScope prof("bwd_finalize", s);
   if ((e = to_bf16(w.dk_acc, a.dk, rows_g * P.d, s)) != hipSuccess) return e;
-  e = to_bf16(w.dv_acc, a.dv, rows_g * P.d, s);
-  prof_end(s);
-  return e;
+  return to_bf16(w.dv_acc, a.dv, rows_g * P.d, s);
 }
 
 }  // namespace msa

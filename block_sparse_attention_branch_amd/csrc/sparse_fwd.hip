@@ -447,16 +447,17 @@ hipError_t run_fwd(const Problem& P, const T* q, const T* k, const T* v, const i
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int s_lo = c0 / span;
     const int s_hi = (c1 == P.N) ? m.nsb : c1 / span;
-    prof_begin("fwd_partial", s);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS, s, q, k, v, block_idx, m.pos,
-                       m.offs, m.rows, m.tiles, po, pl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, s_lo,
-                       s_hi, c0, c1, n_lists, P.scale);
-    prof_end(s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    prof_begin("fwd_merge", s);
-    e = launch_fwd_merge<T, D>(P, po, pl, block_idx, o, lse, c0, CQ, s);
-    prof_end(s);
-    if (e != hipSuccess) return e;
+    {
+      ProfScope prof("fwd_partial", s);
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS, s, q, k, v, block_idx, m.pos,
+                         m.offs, m.rows, m.tiles, po, pl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb, s_lo,
+                         s_hi, c0, c1, n_lists, P.scale);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    {
+      ProfScope prof("fwd_merge", s);
+      if ((e = launch_fwd_merge<T, D>(P, po, pl, block_idx, o, lse, c0, CQ, s)) != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

@@ -408,8 +408,3 @@ def support_size(t: int, block_size: int, topk: int) -> int:
     t mod bs + 1 visible tokens of the own block."""
     return min(topk - 1, t // block_size) * block_size + (t % block_size) + 1
 
-
-def kl_row(pbar: np.ndarray, p_px: np.ndarray) -> float:
-    """KL(pbar || p_px) with 0 log 0 = 0."""
-    nz = pbar > 0
-    return float(np.sum(pbar[nz] * (np.log(pbar[nz]) - np.log(p_px[nz]))))

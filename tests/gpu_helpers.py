@@ -14,7 +14,11 @@ import torch
 import msa_inputs
 from oracle import msa_oracle as O
 
-U32 = 2.0 ** -24
+# Unit roundoff assumed for the matrix unit's fp32 accumulation.  The order
+# and the rounding mode of the sums inside an MFMA instruction are not
+# documented; a directed (truncating) rounding has unit roundoff 2^-23,
+# twice the 2^-24 of round-to-nearest, so the bounds below use 2^-23.
+U_MFMA = 2.0 ** -23
 
 
 def need_gpu():
@@ -47,8 +51,11 @@ def f32(t: torch.Tensor):
     return t.detach().float().cpu().numpy()
 
 
-def gamma(n: int) -> float:
-    return n * U32 / (1 - n * U32)
+def gamma(n: int, u: float = U_MFMA) -> float:
+    """Higham's gamma_n = n u / (1 - n u): an n-term dot product computed in
+    floating point (products and sums rounded, any order) differs from the
+    exact one by at most gamma_n * sum_i |x_i y_i|."""
+    return n * u / (1 - n * u)
 
 
 def selection_equivalent(gpu_sel, ref_sel, ref_pooled_row, t, block_size, tol):
@@ -71,13 +78,37 @@ def selection_equivalent(gpu_sel, ref_sel, ref_pooled_row, t, block_size, tol):
     return all(abs(a - b) <= tol for a, b in zip(gv, rv))
 
 
-def row_tolerance(q_idx_row, k_idx_b, t, causal, d_idx):
-    """2 * gamma_{d_idx} * max_u sum_i |q_i k_i|: how far an fp32-accumulated
-    index score may sit from the exact one (Higham's bound), doubled for the
-    two scores compared."""
+def score_bound(q_idx_row, k_idx_b, t, causal, d_idx):
+    """gamma_{d_idx} * max_u sum_i |q_i k_i| over the row's visible keys: how
+    far an fp32-accumulated index score, and so a block max of such scores,
+    may sit from the exact value."""
     a = np.abs(np.asarray(q_idx_row, dtype=np.float64))
     kk = np.abs(np.asarray(k_idx_b[: t + 1] if causal else k_idx_b, dtype=np.float64))
-    return 2.0 * gamma(d_idx) * float((kk @ a).max())
+    return gamma(d_idx) * float((kk @ a).max())
+
+
+def score_bounds(q_idx_b, k_idx_b, causal, d_idx, chunk=256):
+    """score_bound of every row of one batch entry at once: q_idx_b [N, H_kv,
+    d_idx], k_idx_b [N, d_idx] -> [N, H_kv]."""
+    a = np.abs(np.asarray(q_idx_b, dtype=np.float64))
+    kk = np.abs(np.asarray(k_idx_b, dtype=np.float64))
+    N = a.shape[0]
+    out = np.empty(a.shape[:2])
+    for t0 in range(0, N, chunk):
+        t1 = min(t0 + chunk, N)
+        m = np.einsum("thi,ui->thu", a[t0:t1], kk)
+        if causal:
+            hidden = np.arange(t1 - t0)[:, None] + t0 < np.arange(N)[None, :]    # u > t
+            m[np.broadcast_to(hidden[:, None, :], m.shape)] = 0.0
+        out[t0:t1] = m.max(axis=2)
+    return gamma(d_idx) * out
+
+
+def row_tolerance(q_idx_row, k_idx_b, t, causal, d_idx):
+    """Largest gap between two blocks' exact pooled scores that the GPU may
+    order the other way: each pooled score may move by score_bound, so twice
+    that."""
+    return 2.0 * score_bound(q_idx_row, k_idx_b, t, causal, d_idx)
 
 
 def sample_rows(B, N, n, seed, extra=()):

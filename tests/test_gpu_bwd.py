@@ -2,9 +2,18 @@
 block_idx.
 
 Bar: every gradient tensor (dq, dk, dv, dq_idx, dk_idx) and dscore at cosine
->= 0.999 against the fp64 oracle (max-relative error reported); the KL value
-per row within 2e-2 absolute.  Properties checked at any size: per row the
-index-logit gradient sums to zero (sum p_px = sum pbar = 1)."""
+>= 0.999 against the fp64 oracle, both over the whole tensor and on every
+slice where a local error would hide: per (query row, group) for dq, dq_idx
+and dscore, per (KV block, group) for dk and dv, per KV block for dk_idx.  A
+slice whose oracle value is zero must be (near) zero on the GPU too.  The KL
+value per row within 2e-2 absolute.  Properties checked at any size: per row
+the index-logit gradient sums to zero (sum p_px = sum pbar = 1).
+
+At the full sizes (8K with B = 4, 128K, 1M) the heavy-list tests compare the
+whole dk, dv and dk_idx tensors: off a seeded sample of rows dO and q_idx are
+zero, so only the sampled rows add to them (exactly zero elsewhere), while
+those zero index queries make every row select blocks 0 .. topk-2, whose
+inverted lists then span many work items (and every main-kernel chunk)."""
 
 import numpy as np
 import pytest
@@ -12,18 +21,25 @@ import torch
 
 import msa_inputs
 from oracle import msa_oracle as O
-from tests.gpu_helpers import bwd_chunk_queries, cosine, f32, max_rel, need_gpu, sample_rows, say
+from tests.gpu_helpers import bwd_chunk_queries, cosine, f32, fwd_chunk_queries, max_rel, need_gpu, \
+    sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
 COS = 0.999
+DEV = "cuda"   # device of the test tensors
+# A slice whose oracle value is exactly zero may hold rounding residue on the
+# GPU (e.g. t = 0, where p_px = pbar = 1 in exact arithmetic): it must stay
+# below this fraction of the largest slice norm of the tensor.
+ZERO_FRAC = 1e-4
 
 
-def _run(w, variant="normal", causal=True, want_dscore=False, want_kl=False, lam=1.0):
+def _run(w, variant="normal", causal=True, want_dscore=False, want_kl=False, lam=1.0, x=None):
     msa = need_gpu()
     say(f"[bwd] {w.name} variant={variant} causal={causal} B={w.B} N={w.N} H={w.H_q}/{w.H_kv} d={w.d} "
         f"d_idx={w.d_idx} topk={w.topk}")
-    x = msa_inputs.make_inputs(w, variant, device="cuda", with_grad_out=True)
+    if x is None:
+        x = msa_inputs.make_inputs(w, variant, device="cuda", with_grad_out=True)
     sel = msa.index_topk(x["q_idx"], x["k_idx"], topk=w.topk, causal=causal)
     o, lse = msa.sparse_fwd(x["q"], x["k"], x["v"], sel, d_idx=w.d_idx, causal=causal)
     gr = msa.sparse_bwd(x["q"], x["k"], x["v"], o, x["dO"], lse, sel, x["q_idx"], x["k_idx"], kl_weight=lam,
@@ -32,11 +48,50 @@ def _run(w, variant="normal", causal=True, want_dscore=False, want_kl=False, lam
     return x, sel, gr
 
 
+def _slices_cos(name, got, ref, what, cos_min=COS, norm_scale=None):
+    """got, ref: [S, L] (one slice per row).  cos >= cos_min on every slice
+    with a nonzero reference; near zero where the reference is zero."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    rn = np.sqrt((r * r).sum(axis=1))
+    gn = np.sqrt((g * g).sum(axis=1))
+    scale = float(rn.max()) if norm_scale is None else norm_scale
+    live = rn > 0
+    cos = (g[live] * r[live]).sum(axis=1) / np.maximum(gn[live] * rn[live], 1e-300)
+    worst = float(cos.min()) if cos.size else 1.0
+    zero_res = float(gn[~live].max()) / scale if (~live).any() and scale > 0 else 0.0
+    say(f"  {name:9s} per {what}: {int(live.sum())} slices, worst cos {worst:.6f}; "
+        f"{int((~live).sum())} zero slices, largest residue {zero_res:.1e} of the top norm")
+    if cos.size:
+        i = int(np.argmin(cos))
+        assert worst >= cos_min, (name, what, "slice", int(np.nonzero(live)[0][i]), worst)
+    assert zero_res <= ZERO_FRAC, (name, what, "nonzero where the oracle is zero", zero_res)
+
+
 def _cmp(name, got, ref, cos_min=COS):
     c, r = cosine(got, ref), max_rel(got, ref)
-    say(f"  {name:7s} cos {c:.6f} maxrel {r:.3e}")
+    say(f"  {name:9s} cos {c:.6f} maxrel {r:.3e}")
     assert c >= cos_min, name
     return c
+
+
+def _per_row_group(a, H_kv):
+    """[..., H(_q or _kv), X] rows -> [rows * H_kv, rest]: one slice per (row, group)."""
+    a = np.asarray(a)
+    lead = int(np.prod(a.shape[: a.ndim - 2])) if a.ndim > 2 else 1
+    return a.reshape(lead * H_kv, -1)
+
+
+def _per_block_group(a, bs):
+    """[B, N, H_kv, d] -> [(b, j, g), bs * d]."""
+    B, N, H, D = a.shape
+    return np.asarray(a).reshape(B, N // bs, bs, H, D).transpose(0, 1, 3, 2, 4).reshape(-1, bs * D)
+
+
+def _per_block(a, bs):
+    """[B, N, d_idx] -> [(b, j), bs * d_idx]."""
+    B, N, D = a.shape
+    return np.asarray(a).reshape(B * (N // bs), bs * D)
 
 
 def _full(w, causal=True, lam=1.0):
@@ -44,13 +99,23 @@ def _full(w, causal=True, lam=1.0):
     h = {k: f32(v) for k, v in x.items()}
     ref = O.sparse_bwd(h["q"], h["k"], h["v"], h["dO"], h["q_idx"], h["k_idx"],
                        sel.cpu().numpy().astype(np.int64), w.block_size, causal, kl_weight=lam, want_dscore=True)
-    for name in ("dq", "dk", "dv", "dq_idx", "dk_idx", "dscore"):
-        _cmp(name, f32(gr[name]), ref[name])
+    got = {n: f32(gr[n]) for n in ("dq", "dk", "dv", "dq_idx", "dk_idx", "dscore")}
+    for name in got:
+        _cmp(name, got[name], ref[name])
+    bs, H = w.block_size, w.H_kv
+    _slices_cos("dq", _per_row_group(got["dq"].reshape(w.B, w.N, H, -1), H),
+                _per_row_group(ref["dq"].reshape(w.B, w.N, H, -1), H), "(row, group)")
+    _slices_cos("dq_idx", _per_row_group(got["dq_idx"], H), _per_row_group(ref["dq_idx"], H), "(row, group)")
+    _slices_cos("dscore", got["dscore"].reshape(w.B * w.N * H, -1), ref["dscore"].reshape(w.B * w.N * H, -1),
+                "(row, group)")
+    for name in ("dk", "dv"):
+        _slices_cos(name, _per_block_group(got[name], bs), _per_block_group(ref[name], bs), "(block, group)")
+    _slices_cos("dk_idx", _per_block(got["dk_idx"], bs), _per_block(ref["dk_idx"], bs), "block")
     dkl = float(np.abs(f32(gr["kl"]) - ref["kl"]).max())
     say(f"  kl maxabs {dkl:.3e}")
     assert dkl <= 2e-2
     # Property: per (b, t, g) the index-logit gradient sums to zero.
-    zsum = f32(gr["dscore"]).sum(axis=(3, 4))
+    zsum = got["dscore"].sum(axis=(3, 4))
     assert np.abs(zsum).max() <= 1e-3 * max(1.0, abs(lam))
 
 
@@ -96,44 +161,64 @@ def test_bwd_multi_tile_full():
     _full(w)
 
 
+def _seams(w):
+    """Rows on both sides of every launch seam of the forward and of the
+    backward main kernel."""
+    out = []
+    for chunk in (fwd_chunk_queries(w), bwd_chunk_queries(w)):
+        out += [c + dt for c in range(chunk, w.N, chunk) for dt in (-1, 0, 1)]
+    return out
+
+
+def _check_rows(w, gr, ref, bt):
+    H = w.H_kv
+    dq = f32(gr["dq"][bt[:, 0], bt[:, 1]])
+    dqi = f32(gr["dq_idx"][bt[:, 0], bt[:, 1]])
+    _cmp("dq", dq, ref["dq"])
+    _cmp("dq_idx", dqi, ref["dq_idx"])
+    _slices_cos("dq", _per_row_group(dq.reshape(len(bt), H, -1), H),
+                _per_row_group(ref["dq"].reshape(len(bt), H, -1), H), "(row, group)")
+    _slices_cos("dq_idx", _per_row_group(dqi, H), _per_row_group(ref["dq_idx"], H), "(row, group)")
+
+
 def _sampled(w, variant, n_rows, seed, blocks):
-    """Rows: dq, dq_idx, kl, dscore of sampled rows.  Blocks: dk, dv (group 0)
-    and dk_idx of sampled KV blocks of batch 0, recomputed from every row that
-    selected them."""
+    """Rows: dq, dq_idx, kl of sampled rows.  Blocks: dk, dv and dk_idx of
+    sampled KV blocks of batch 0, recomputed from every row that selected
+    them."""
     x, sel, gr = _run(w, variant, want_kl=True)
-    chunk = bwd_chunk_queries(w)
-    seams = [c + dt for c in range(chunk, w.N, chunk) for dt in (-1, 0, 1)]
+    seams = _seams(w)
     rows = sample_rows(w.B, w.N, n_rows, seed, extra=seams)
-    say(f"  main-kernel chunk {chunk} queries, {len(seams)} seam rows")
+    say(f"  {len(seams)} seam rows")
     bt = torch.tensor(rows, dtype=torch.long)
     s = sel.cpu().numpy().astype(np.int64)
     k_h, v_h, ki_h = f32(x["k"]), f32(x["v"]), f32(x["k_idx"])
     ref = O.sparse_bwd(f32(x["q"][bt[:, 0], bt[:, 1]]), k_h, v_h, f32(x["dO"][bt[:, 0], bt[:, 1]]),
                        f32(x["q_idx"][bt[:, 0], bt[:, 1]]), ki_h, s, w.block_size, True, rows=rows)
-    _cmp("dq", f32(gr["dq"][bt[:, 0], bt[:, 1]]), ref["dq"])
-    _cmp("dq_idx", f32(gr["dq_idx"][bt[:, 0], bt[:, 1]]), ref["dq_idx"])
+    _check_rows(w, gr, ref, bt)
     dkl = float(np.abs(f32(gr["kl"][bt[:, 0], bt[:, 1]]) - ref["kl"]).max())
     say(f"  kl maxabs {dkl:.3e} over {len(rows)} rows")
     assert dkl <= 2e-2
+    bs = w.block_size
     for j in blocks:
         sel_rows = np.nonzero((s[0] == j).any(axis=(1, 2)))[0]
         brow = [(0, int(t)) for t in sel_rows]
         bti = torch.tensor(brow, dtype=torch.long)
         say(f"  block {j}: {len(brow)} selecting rows")
         rb = O.sparse_bwd(f32(x["q"][bti[:, 0], bti[:, 1]]), k_h, v_h, f32(x["dO"][bti[:, 0], bti[:, 1]]),
-                          f32(x["q_idx"][bti[:, 0], bti[:, 1]]), ki_h, s, w.block_size, True, rows=brow)
-        ks = slice(j * w.block_size, (j + 1) * w.block_size)
+                          f32(x["q_idx"][bti[:, 0], bti[:, 1]]), ki_h, s, bs, True, rows=brow)
+        ks = slice(j * bs, (j + 1) * bs)
         for name in ("dk", "dv"):
-            _cmp(f"{name}[{j}]", f32(gr[name][0, ks]), rb[name][0, ks])
+            g_, r_ = f32(gr[name][0, ks]), rb[name][0, ks]
+            _cmp(f"{name}[{j}]", g_, r_)
+            _slices_cos(f"{name}[{j}]", g_.transpose(1, 0, 2).reshape(w.H_kv, -1),
+                        r_.transpose(1, 0, 2).reshape(w.H_kv, -1), "group")
         _cmp(f"dki[{j}]", f32(gr["dk_idx"][0, ks]), rb["dk_idx"][0, ks])
 
 
 # The sampled KV blocks are late ones, chosen by a few hundred to about a
-# thousand rows, so the fp64 recomputation of their dk/dv stays within seconds
-# (block 5 at 8K is chosen by ~7300 rows: minutes).  Lists long enough to
-# span several work items, whose dk/dv add up across items, are compared in
-# full by test_bwd_multi_tile_full (its longest lists hold ~1550 entries past
-# the own block, beyond one item's 1024).
+# thousand rows, so the fp64 recomputation of their dk/dv stays within seconds.
+# Long lists that span many work items and chunks are compared in full by the
+# heavy-list tests below.
 def test_bwd_b4_8k_sampled():
     w = msa_inputs.WORKLOADS["fwdbwd-bf16-b4-n8k"]
     _sampled(w, "normal", 96, 3, blocks=[w.nblk - 1, w.nblk - 8])
@@ -152,6 +237,107 @@ def test_bwd_128k_planted_sampled():
 def test_bwd_1m_sampled():
     w = msa_inputs.WORKLOADS["fwdbwd-bf16-n1m"]
     _sampled(w, "normal", 16, 5, blocks=[w.nblk - 1])
+
+
+PLANT = 10.0
+
+
+def _heavy_inputs(w, rows, seed):
+    """The workload's N(0,1) tensors, then: off the sampled rows, dO = 0 and
+    q_idx = 0; on them, q_idx gets a seeded unit direction c with weight
+    PLANT (its component along c replaced), and the index keys of block 0 get
+    + PLANT c, so every sampled row past block 0 also selects block 0."""
+    x = msa_inputs.make_inputs(w, "normal", device=DEV, with_grad_out=True)
+    keep = torch.zeros((w.B, w.N), dtype=torch.bool, device=DEV)
+    bt = torch.tensor(rows, dtype=torch.long, device=DEV)
+    keep[bt[:, 0], bt[:, 1]] = True
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    c = torch.randn((w.d_idx,), generator=gen, device=DEV, dtype=torch.float32)
+    c = c / c.norm()
+    qi = x["q_idx"].float()
+    qi = qi - (qi @ c)[..., None] * c + PLANT * c
+    x["q_idx"] = torch.where(keep[:, :, None, None], qi, 0.0).to(x["q_idx"].dtype)
+    ki = x["k_idx"].float()
+    ki[:, : w.block_size] += PLANT * c
+    x["k_idx"] = ki.to(x["k_idx"].dtype)
+    x["dO"] = torch.where(keep[:, :, None, None], x["dO"], torch.zeros_like(x["dO"]))
+    return x
+
+
+def _heavy(w, n_rows, seed):
+    rows = sample_rows(w.B, w.N, n_rows, seed, extra=_seams(w))
+    x = _heavy_inputs(w, rows, seed)
+    x, sel, gr = _run(w, "normal", x=x)
+    bs, H = w.block_size, w.H_kv
+    # The construction: every row past block 0 selected block 0, so block 0's
+    # list holds N - bs entries per (batch, group).
+    t = torch.arange(w.N, device=DEV)
+    assert bool((sel == 0).any(dim=-1)[:, t >= bs].all()), "block 0 must be in every row's selection"
+    lens = [int((sel[:, bs:] == j).any(dim=-1).sum()) for j in (0, 1, w.topk - 2)]
+    say(f"  {len(rows)} sampled rows; list lengths over (batch, group) of blocks 0, 1, {w.topk - 2}: {lens}")
+    bt = torch.tensor(rows, dtype=torch.long)
+    s = sel.cpu().numpy().astype(np.int64)
+    ref = O.sparse_bwd(f32(x["q"][bt[:, 0], bt[:, 1]]), f32(x["k"]), f32(x["v"]), f32(x["dO"][bt[:, 0], bt[:, 1]]),
+                       f32(x["q_idx"][bt[:, 0], bt[:, 1]]), f32(x["k_idx"]), s, bs, True, rows=rows)
+    _check_rows(w, gr, ref, bt)
+    # dk, dv per (batch, block, group); dk_idx per (batch, block).  Only
+    # slices some sampled row selected can be nonzero: those are compared with
+    # the oracle on the host; every other slice must be exactly zero, which is
+    # checked on the device over the whole tensor.
+    nblk = w.N // bs
+    touched = np.zeros((w.B, nblk, H), dtype=bool)
+    for (b, t_) in rows:
+        for g in range(H):
+            js = s[b, t_, g]
+            touched[b, js[js >= 0], g] = True
+    touched_b = touched.any(axis=2)
+    tb = torch.from_numpy(touched).to(DEV)
+    for name in ("dk", "dv"):
+        a = gr[name].view(w.B, nblk, bs, H, w.d).float().abs().amax(dim=(2, 4))     # [B, nblk, H]
+        resid = float(torch.where(tb, torch.zeros_like(a), a).max())
+        say(f"  {name}: {int(touched.sum())} touched (block, group) slices; largest value elsewhere {resid}")
+        assert resid == 0.0, name
+        idx = np.argwhere(touched)
+        ii = torch.from_numpy(idx).to(DEV)
+        g_ = f32(gr[name].view(w.B, nblk, bs, H, w.d)[ii[:, 0], ii[:, 1], :, ii[:, 2]]).reshape(len(idx), -1)
+        r_ = ref[name].reshape(w.B, nblk, bs, H, w.d)[idx[:, 0], idx[:, 1], :, idx[:, 2]].reshape(len(idx), -1)
+        _cmp(name, g_, r_)
+        _slices_cos(name, g_, r_, "(block, group)")
+        j0 = np.nonzero((idx[:, 1] == 0))[0]
+        _slices_cos(f"{name}[0]", g_[j0], r_[j0], "(batch, group) of block 0")
+    a = gr["dk_idx"].view(w.B, nblk, bs * w.d_idx).abs().amax(dim=2)
+    tbb = torch.from_numpy(touched_b).to(DEV)
+    resid = float(torch.where(tbb, torch.zeros_like(a), a).max())
+    say(f"  dk_idx: {int(touched_b.sum())} touched blocks; largest value elsewhere {resid}")
+    assert resid == 0.0
+    idx = np.argwhere(touched_b)
+    ii = torch.from_numpy(idx).to(DEV)
+    g_ = f32(gr["dk_idx"].view(w.B, nblk, bs * w.d_idx)[ii[:, 0], ii[:, 1]])
+    r_ = ref["dk_idx"].reshape(w.B, nblk, bs * w.d_idx)[idx[:, 0], idx[:, 1]]
+    _cmp("dk_idx", g_, r_)
+    _slices_cos("dk_idx", g_, r_, "block")
+
+
+def test_bwd_b4_8k_heavy_lists():
+    # Block 0's list: 8064 entries per (batch, group), eight main-kernel items.
+    _heavy(msa_inputs.WORKLOADS["fwdbwd-bf16-b4-n8k"], 64, 31)
+
+
+def test_bwd_128k_heavy_lists():
+    # 131,008 entries per group in each of the lists of blocks 0 .. 14: about
+    # 128 work items each, all adding into the same dk / dv / dk_idx rows.
+    _heavy(msa_inputs.WORKLOADS["fwdbwd-bf16-n128k"], 160, 41)
+
+
+def test_bwd_1m_heavy_lists_across_chunks():
+    # Block 0's list spans every main-kernel chunk (4 at this size), and the
+    # sampled rows sit in all of them, so its dk / dv / dk_idx add up across
+    # launches.
+    w = msa_inputs.WORKLOADS["fwdbwd-bf16-n1m"]
+    chunk = bwd_chunk_queries(w)
+    say(f"  main-kernel chunk {chunk} queries: {(w.N + chunk - 1) // chunk} launches")
+    _heavy(w, 64, 51)
 
 
 def test_bwd_dq_and_forward_deterministic():
