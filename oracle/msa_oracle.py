@@ -304,14 +304,18 @@ def sparse_fwd_recurrence(q, k, v, block_idx, block_size: int, causal: bool = Tr
 def sparse_bwd(q, k, v, dO, q_idx, k_idx, block_idx, block_size: int,
                causal: bool = True, scale: float | None = None,
                scale_idx: float | None = None, kl_weight: float = 1.0,
-               rows=None, want_dscore: bool = False):
+               rows=None, want_dscore: bool = False, o=None):
     """Gradients of the main branch plus the KL-alignment gradient of the index
     branch, all on the selected support.
 
     Main branch ([FA] "Training and the backward pass"): rebuild P from the
     scores, dV += P^T dO, dP = dO V^T; the softmax Jacobian gives
-    dS = P * (dP - sum_u P dP), then dQ = scale dS K and dK += scale dS^T Q.
-    dK and dV of a group sum over its G heads.
+    dS = P * (dP - D) with D = sum_u P dP, then dQ = scale dS K and
+    dK += scale dS^T Q.  dK and dV of a group sum over its G heads.
+    When the forward's output `o` is given (as the backward receives it,
+    [B,N,H_q,d] or compact per row), D is the row sum of dO * o, the way the
+    FlashAttention backward forms it from the stored output; in exact
+    arithmetic the two are equal (o = sum_u P v_u, so dO . o = sum_u P dP).
 
     Index branch ([FMSA] "Removing the KL-divergence bottleneck"; [MSA]
     "Training sparse attention"): teacher pbar = mean over the group's heads of
@@ -353,6 +357,7 @@ def sparse_bwd(q, k, v, dO, q_idx, k_idx, block_idx, block_size: int,
         qrow = q[i] if compact else q[b, t]
         dorow = dO[i] if compact else dO[b, t]
         qirow = q_idx[i] if compact else q_idx[b, t]
+        orow = None if o is None else (o[i] if compact else o[b, t])
         for g in range(H_kv):
             S = support(block_idx[b, t, g], t, N, block_size, causal)
             hs = slice(g * G, (g + 1) * G)
@@ -360,7 +365,11 @@ def sparse_bwd(q, k, v, dO, q_idx, k_idx, block_idx, block_size: int,
             KS, VS = f64(k[b, S, g]), f64(v[b, S, g])
             _, _, P = _attend(Qg, KS, VS, scale)          # [G, |S|]
             dP = dOg @ VS.T
-            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            if orow is None:
+                D = (P * dP).sum(axis=1, keepdims=True)
+            else:
+                D = (dOg * f64(orow[hs])).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
             dq[i, hs] = scale * dS @ KS
             # S holds distinct keys, so fancy-index accumulation is exact.
             dk[b, S, g] += scale * dS.T @ Qg

@@ -12,7 +12,7 @@ import torch
 
 import msa_inputs
 from oracle import msa_oracle as O
-from tests.gpu_helpers import (f32, need_gpu, row_tolerance, sample_rows, say, score_bounds,
+from tests.gpu_helpers import (U_FP8, U_MFMA, f32, need_gpu, row_tolerance, sample_rows, say, score_bounds,
                                selection_equivalent)
 
 pytestmark = pytest.mark.gpu
@@ -36,6 +36,7 @@ def _run(w, variant, want_pooled=True, causal=True, fp8=False):
 
 
 def _check_full(w, variant, causal=True, exact=True, fp8=False):
+    u = U_FP8 if fp8 else U_MFMA      # unit roundoff of the matrix unit's accumulation
     x, (sel, pooled) = _run(w, variant, True, causal, fp8)
     qi, ki = _host(x["q_idx"]), _host(x["k_idx"])
     ref_sel, ref_pool = O.index_topk(qi, ki, w.block_size, w.topk, causal=causal, want_pooled=True)
@@ -58,7 +59,7 @@ def _check_full(w, variant, causal=True, exact=True, fp8=False):
     # Pooled values: each within the accumulation bound of the row's scores.
     worst = 0.0
     for b in range(w.B):
-        bound = score_bounds(qi[b], ki[b], causal, w.d_idx)                       # [N, H_kv]
+        bound = score_bounds(qi[b], ki[b], causal, w.d_idx, u=u)                  # [N, H_kv]
         err = np.where(fin[b], np.abs(gpool[b].astype(np.float64) - np.where(fin[b], ref_pool[b], 0.0)), 0.0)
         err = err.max(axis=2)
         bad = np.argwhere(err > bound)
@@ -71,7 +72,7 @@ def _check_full(w, variant, causal=True, exact=True, fp8=False):
             for g in range(w.H_kv):
                 if (gsel[b, t, g] == ref_sel[b, t, g]).all():
                     continue
-                tol = row_tolerance(qi[b, t, g], ki[b], t, causal, w.d_idx)
+                tol = row_tolerance(qi[b, t, g], ki[b], t, causal, w.d_idx, u)
                 assert selection_equivalent(gsel[b, t, g], ref_sel[b, t, g], ref_pool[b, t, g], t,
                                             w.block_size, tol), (b, t, g, gsel[b, t, g], ref_sel[b, t, g])
                 flagged += 1
@@ -157,7 +158,7 @@ def _sampled(w, variant, n_rows, seed, fp8=False):
         for g in range(w.H_kv):
             if (gsel[i, g] == ref_sel[i, g]).all():
                 continue
-            tol = row_tolerance(qi_rows[i, g], ki[b], t, True, w.d_idx)
+            tol = row_tolerance(qi_rows[i, g], ki[b], t, True, w.d_idx, U_FP8 if fp8 else U_MFMA)
             assert selection_equivalent(gsel[i, g], ref_sel[i, g], ref_pool[i, g], t, w.block_size, tol), \
                 (b, t, g, gsel[i, g], ref_sel[i, g])
             flagged += 1

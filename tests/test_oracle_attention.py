@@ -267,3 +267,34 @@ def test_sampled_rows_agree_with_full():
     sel_rows = O.index_topk(x["q_idx"], x["k_idx"], x["bs"], x["topk"], rows=rows)
     for i, (b, t) in enumerate(rows):
         assert sel_rows[i].tolist() == x["sel"][b, t].tolist()
+
+
+def test_backward_D_from_the_stored_output():
+    """D = rowsum(dO * o) when the forward's output is passed in, as the
+    FlashAttention backward forms it ('Training and the backward pass').
+    With the exact output it equals sum_u P dP, so every gradient matches the
+    default; an error E in o shifts only the main-branch gradients, by the
+    closed form dS_u -> dS_u - (dO . E) P_u: dq moves by
+    -scale (dO . E) sum_u P_u k_u (sum_u P_u k_u = attention with the keys as
+    values, from torch's SDPA), dv and the index gradients do not move."""
+    x = _case(12, N=48, bs=8, topk=3)
+    args = (x["q"], x["k"], x["v"], x["dO"], x["q_idx"], x["k_idx"], x["sel"], x["bs"], True)
+    base = O.sparse_bwd(*args)
+    o, _ = O.sparse_fwd(x["q"], x["k"], x["v"], x["sel"], x["bs"], True)
+    same = O.sparse_bwd(*args, o=o)
+    for name in ("dq", "dk", "dv", "dq_idx", "dk_idx", "kl"):
+        np.testing.assert_allclose(same[name], base[name], rtol=1e-10, atol=1e-12)
+    rng = np.random.default_rng(3)
+    E = 1e-3 * rng.standard_normal(o.shape)
+    moved = O.sparse_bwd(*args, o=o + E)
+    mask = _brute_mask(x["sel"], x["N"], x["bs"], True)
+    xk = dict(x, v=x["k"])
+    _, _, _, pk = _torch_attention(xk, mask)                                    # B,H,N,d: sum_u P k_u
+    pk = pk.detach().permute(0, 2, 1, 3).numpy()
+    delta = (x["dO"] * E).sum(axis=-1, keepdims=True)                           # B,N,H_q,1
+    scale = 1 / math.sqrt(x["d"])
+    np.testing.assert_allclose(moved["dq"] - base["dq"], -scale * delta * pk, rtol=1e-8, atol=1e-13)
+    np.testing.assert_allclose(moved["dv"], base["dv"], rtol=0, atol=1e-13)
+    for name in ("dq_idx", "dk_idx", "kl"):
+        np.testing.assert_allclose(moved[name], base[name], rtol=0, atol=1e-13)
+    assert np.abs(moved["dk"] - base["dk"]).max() > 1e-6      # dk moves too (by -scale (dO.E) P_u q)
