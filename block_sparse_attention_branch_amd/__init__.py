@@ -5,7 +5,7 @@ of include/msa.h); this package only marshals PyTorch tensors into it.
 """
 
 from .binding import (MsaDims, MsaError, index_topk, load_library, make_dims, profile_collect,
-                      profile_enable, sparse_bwd, sparse_fwd, LIB_PATH)
+                      profile_enable, sparse_bwd, sparse_fwd, sparse_fwd_noalloc, LIB_PATH)
 
 __all__ = ["MsaDims", "MsaError", "index_topk", "load_library", "make_dims", "profile_collect",
-           "profile_enable", "sparse_bwd", "sparse_fwd", "LIB_PATH"]
+           "profile_enable", "sparse_bwd", "sparse_fwd", "sparse_fwd_noalloc", "LIB_PATH"]

@@ -28,7 +28,7 @@ MSA_FP8_E4M3 = 2   # index inputs of msa_index_topk only
 
 EXPORTED = (
     "msa_index_topk_workspace", "msa_index_topk",
-    "msa_sparse_fwd_workspace", "msa_sparse_fwd",
+    "msa_sparse_fwd_workspace", "msa_sparse_fwd", "msa_sparse_fwd_noalloc",
     "msa_sparse_bwd_workspace", "msa_sparse_bwd",
     "msa_status_string", "msa_last_error", "msa_version",
     "msa_profile_enable", "msa_profile_collect",
@@ -69,6 +69,8 @@ def load_library(path: str | None = None):
     lib.msa_sparse_fwd_workspace.restype = sz
     lib.msa_sparse_fwd.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_fwd.restype = i32
+    lib.msa_sparse_fwd_noalloc.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp]
+    lib.msa_sparse_fwd_noalloc.restype = i32
     lib.msa_sparse_bwd_workspace.argtypes = [dims_p]
     lib.msa_sparse_bwd_workspace.restype = sz
     lib.msa_sparse_bwd.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
@@ -209,6 +211,30 @@ def sparse_fwd(q, k, v, block_idx, d_idx: int = 64, block_size: int = 128, causa
     st = lib.msa_sparse_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(o),
                             _ptr(lse), _ptr(ws), ws_n, _stream(q.device))
     _check(lib, st, "msa_sparse_fwd")
+    return o, lse
+
+
+def sparse_fwd_noalloc(q, k, v, block_idx, o, lse, d_idx: int = 64, block_size: int = 128,
+                       causal: bool = True, scale: float | None = None):
+    """msa_sparse_fwd_noalloc: the forward into caller-given o [B,N,H_q,d]
+    (dtype of q) and lse [B,N,H_q] fp32, with the library's fixed device
+    scratch instead of a workspace.  Nothing is allocated here."""
+    _shapes({"q": ("B", "N", "H_q", "d"), "k": ("B", "N", "H_kv", "d"), "v": ("B", "N", "H_kv", "d"),
+             "block_idx": ("B", "N", "H_kv", "topk"), "o": ("B", "N", "H_q", "d"), "lse": ("B", "N", "H_q")},
+            q=q, k=k, v=v, block_idx=block_idx, o=o, lse=lse)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _need(t, n, q.dtype)
+    _need(block_idx, "block_idx", torch.int32)
+    _need(lse, "lse", torch.float32)
+    lib = load_library()
+    B, N, H_q, d = q.shape
+    H_kv = k.shape[2]
+    topk = block_idx.shape[3]
+    dims = make_dims(B, N, H_q, H_kv, d, d_idx, block_size, topk, causal, _dtype_code(q), scale or 0.0)
+    with torch.cuda.device(q.device):
+        st = lib.msa_sparse_fwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx),
+                                        _ptr(o), _ptr(lse), _stream(q.device))
+    _check(lib, st, "msa_sparse_fwd_noalloc")
     return o, lse
 
 

@@ -14,6 +14,13 @@
 
 #include "msa_internal.h"
 
+// Fixed device scratch of msa_sparse_fwd_noalloc: the block map and the
+// forward partials of one query chunk.  Each device holds its own copy from
+// the moment the library's code object is loaded there until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// array: kernels and copies take the address from scratch_ptr() instead.
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -130,6 +137,58 @@ int fwd_chunk_queries(const msa::Problem& P) {
   if (q < span) q = span;
   if (q >= (size_t)P.N) q = P.N;
   return (int)q;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device with hipGetSymbolAddress while that device is current.
+int scratch_ptr(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_fwd_noalloc: device %d (at most %d devices)", dev, kMaxDevices);
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "msa_sparse_fwd_noalloc: hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(MSA_ERR_INVALID_ARG, "msa_sparse_fwd_noalloc: the stream belongs to device %d, device %d is current",
+                  (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "msa_sparse_fwd_noalloc: hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MSA_ERR_HIP, "msa_sparse_fwd_noalloc: scratch has no device address");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MSA_OK;
+}
+
+// Query chunk of the forward when the block map and the partials must share
+// `cap` bytes: the default chunk if its partials fit beside the map, else the
+// largest multiple of the super-block span that does; 0 when not even one
+// span fits.
+int fwd_chunk_within(const msa::Problem& P, size_t map_bytes, size_t cap) {
+  if (map_bytes >= cap) return 0;
+  auto fits = [&](int c) { return map_bytes + align_up(msa::sparse_fwd_partials_bytes(P, c)) <= cap; };
+  const int chunk = fwd_chunk_queries(P);
+  if (fits(chunk)) return chunk;
+  const int span = msa::block_map_super_span(P);
+  const size_t esz = P.dtype == MSA_BF16 ? 2 : 4;
+  const size_t per_query = (size_t)P.B * P.H_q * P.topk * (P.d * esz + sizeof(float));
+  size_t c = (cap - map_bytes) / per_query;
+  if (c > (size_t)chunk) c = chunk;
+  c -= c % span;
+  // Each of the partials' two regions is rounded up to 256 bytes.
+  while (c > 0 && !fits((int)c)) c -= span;
+  return (int)c;
 }
 
 // Kernel timing (see msa_profile_enable in msa.h).
@@ -297,6 +356,39 @@ MSA_API int msa_sparse_fwd(const msa_dims* dims, const void* q, const void* k, c
   e = msa::launch_sparse_fwd(P, q, k, v, block_idx, o, lse, m, static_cast<char*>(workspace) + map_bytes,
                              chunk, s);
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_fwd launch");
+  return ok();
+}
+
+MSA_API int msa_sparse_fwd_noalloc(const msa_dims* dims, const void* q, const void* k, const void* v,
+                                   const int32_t* block_idx, void* o, float* lse, void* stream) {
+  msa::Problem P;
+  int st = check_dims(dims, &P);
+  if (st != MSA_OK) return st;
+  if ((st = check_main_dtype(P)) != MSA_OK) return st;
+  REQUIRE(q);
+  REQUIRE(k);
+  REQUIRE(v);
+  REQUIRE(block_idx);
+  REQUIRE(o);
+  REQUIRE(lse);
+  const size_t map_bytes = align_up(msa::block_map_bytes(P));
+  const int chunk = fwd_chunk_within(P, map_bytes, MSA_NOALLOC_SCRATCH_BYTES);
+  if (chunk == 0)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "msa_sparse_fwd_noalloc: the block map (%zu bytes) and the partials of %d queries (%zu bytes) "
+                "exceed the fixed scratch of %zu bytes; use msa_sparse_fwd with a workspace",
+                map_bytes, msa::block_map_super_span(P),
+                align_up(msa::sparse_fwd_partials_bytes(P, msa::block_map_super_span(P))),
+                (size_t)MSA_NOALLOC_SCRATCH_BYTES);
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(s, &ws)) != MSA_OK) return st;
+  msa::BlockMap m;
+  msa::block_map_carve(P, ws, &m);
+  hipError_t e = msa::launch_block_map(P, block_idx, m, 0, s);
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_fwd_noalloc block map");
+  e = msa::launch_sparse_fwd(P, q, k, v, block_idx, o, lse, m, static_cast<char*>(ws) + map_bytes, chunk, s);
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_fwd_noalloc launch");
   return ok();
 }
 

@@ -16,9 +16,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensor pointers are DEVICE pointers to caller-owned, contiguous,
- *    row-major buffers, 16-byte aligned.  The library never allocates, frees
- *    or synchronises; every call only enqueues work on `stream` (a
- *    hipStream_t passed as void*; NULL means the default stream) and returns.
+ *    row-major buffers, 16-byte aligned.  The library never calls an
+ *    allocator, frees or synchronises; every call only enqueues work on
+ *    `stream` (a hipStream_t passed as void*; NULL means the default stream)
+ *    and returns.  Its one device array of its own (the scratch of
+ *    msa_sparse_fwd_noalloc) comes with its code object on each device.
  *  - Layouts ([FA] "Tiling mechanism" gives per-head Q, K, V of N rows and d
  *    columns; heads are stacked innermost-but-one):
  *        q, o, dO, dq      [B, N, H_q,  d]
@@ -144,6 +146,33 @@ MSA_API size_t msa_sparse_fwd_workspace(const msa_dims* dims);
 MSA_API int msa_sparse_fwd(const msa_dims* dims, const void* q, const void* k, const void* v,
                            const int32_t* block_idx, void* o, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * msa_sparse_fwd without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation.  Same arguments (minus the workspace), same
+ * results: o and lse equal msa_sparse_fwd's bit for bit.
+ *
+ * The block map and the partial results live in one fixed device array of
+ * MSA_NOALLOC_SCRATCH_BYTES inside the library; each device that runs this
+ * call holds its own copy from the first call until the process ends.  When
+ * the partials of all queries do not fit, queries run in more launches.
+ * Nothing in the array needs clearing between calls (every launch writes
+ * what it later reads), and no hipMemset is issued.
+ *   - Device: the current device; `stream` must belong to it.  The first
+ *     call on a device looks the array's address up there.
+ *   - Rejected with MSA_ERR_UNSUPPORTED, before any launch, when the block
+ *     map plus the partials of one super-block of queries exceed the array
+ *     (for N = 128K with H_kv = 8, topk = 16, the block map alone needs
+ *     64 MiB).  Other errors as msa_sparse_fwd.
+ *   - Calls that overlap in time on one device race on the array: order
+ *     them on one stream (or otherwise serialise them).
+ * Allocates no device or host memory (with kernel timing, msa_profile_enable,
+ * left off).
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+MSA_API int msa_sparse_fwd_noalloc(const msa_dims* dims, const void* q, const void* k, const void* v,
+                                   const int32_t* block_idx, void* o, float* lse, void* stream);
 
 /*
  * Fused backward of both branches.  [FA] "Training and the backward pass"

@@ -79,6 +79,7 @@ def test_invalid_dims_rejected_by_every_entry_point(lib, kw, expect):
     assert lib.msa_index_topk(d, FAKE, FAKE, FAKE, NULL, NULL, 0, NULL) == expect
     assert lib.msa_last_error().decode() != ""
     assert lib.msa_sparse_fwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL) == expect
+    assert lib.msa_sparse_fwd_noalloc(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == expect
     assert lib.msa_sparse_bwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE,
                               FAKE, FAKE, FAKE, NULL, NULL, FAKE, 1 << 40, NULL) == expect
     assert lib.msa_index_topk_workspace(d) == 0
@@ -156,3 +157,24 @@ def test_fp8_only_for_the_index_branch(lib):
     assert lib.msa_index_topk(ctypes.byref(d8), NULL, FAKE, FAKE, NULL, NULL, 0, NULL) == bnd.MSA_ERR_INVALID_ARG
     bad = good_dims(dtype=7)
     assert lib.msa_index_topk(ctypes.byref(bad), FAKE, FAKE, FAKE, NULL, NULL, 0, NULL) == bnd.MSA_ERR_INVALID_ARG
+
+
+def test_noalloc_forward_validates_like_the_forward(lib):
+    d = ctypes.byref(good_dims())
+    for missing in range(6):
+        a = [FAKE] * 6
+        a[missing] = NULL
+        assert lib.msa_sparse_fwd_noalloc(d, *a, NULL) == bnd.MSA_ERR_INVALID_ARG, missing
+    d8 = good_dims(dtype=bnd.MSA_FP8_E4M3)
+    assert lib.msa_sparse_fwd_noalloc(ctypes.byref(d8), *([FAKE] * 6), NULL) == bnd.MSA_ERR_UNSUPPORTED
+
+
+def test_noalloc_forward_rejects_problems_beyond_its_scratch(lib):
+    # N = 128K with 64/8 heads and topk 16: the block map alone is about
+    # 98 MiB and one super-block of partials 34 MiB more, past the 128 MiB
+    # the library holds; refused before any HIP call.
+    dims = good_dims(N=1 << 17, H_q=64, H_kv=8, topk=16)
+    st = lib.msa_sparse_fwd_noalloc(ctypes.byref(dims), *([FAKE] * 6), NULL)
+    assert st == bnd.MSA_ERR_UNSUPPORTED
+    msg = lib.msa_last_error().decode()
+    assert "scratch" in msg and str(128 << 20) in msg
