@@ -11,16 +11,18 @@
 // execution' (the proxy pass accumulates no output, only scores and top-k
 // indices, kept in registers).
 //
-// Work split.  A workgroup of 8 waves streams the index keys of one batch
-// row block by block (128 keys per block, staged in LDS, double buffered).
-// Each wave owns 64 queries of one group.  For a block it computes the
+// Work split.  A workgroup of 4 waves streams the index keys of one batch
+// row block by block (128 keys per block, staged in LDS, double buffered);
+// two workgroups share a CU, so one's products run while the other waits at
+// its barrier or pools.  Each wave owns 64 queries of one group.  For a block it computes the
 // 128 x 64 score tile as S^T = K_idx Q_idx^T with 32x32 MFMA tiles: keys are
 // the tile rows, queries the columns, so a lane holds one query and 16 keys
 // per tile and the block max is a register max plus one exchange between the
 // two half-waves.  After the exchange lane l owns query q0 + l and folds the
 // block's pooled score into its sorted list of the best topk-1 other blocks
-// (strictly greater wins, so equal scores keep the lower block index).  No
-// pooled score ever reaches HBM unless the caller asks for it.
+// (strictly greater wins, so equal scores keep the lower block index),
+// through a per-lane candidate filter that keeps most blocks off the list.
+// No pooled score ever reaches HBM unless the caller asks for it.
 #include <float.h>
 #include <limits.h>
 
@@ -29,9 +31,12 @@
 namespace msa {
 namespace {
 
-constexpr int kIdxWaves = 8;
+constexpr int kIdxWaves = 4;
 constexpr int kIdxThreads = kIdxWaves * kWave;
 constexpr int kQPerWave = 64;
+// Candidate slots per lane: blocks whose pooled score passes the lane's
+// threshold wait here until one lane's slots are full, then join the list.
+constexpr int kCandSlots = 8;
 
 template <typename T, int DIDX>
 struct IdxCfg {
@@ -42,7 +47,9 @@ struct IdxCfg {
   static constexpr int CHUNKS_PER_ROW = DIDX * (int)sizeof(T) / 16;
   static constexpr int CHUNKS_PER_THREAD = kBlock * CHUNKS_PER_ROW / kIdxThreads;
   static_assert(kBlock * CHUNKS_PER_ROW % kIdxThreads == 0, "tile load must split evenly");
-  static constexpr size_t LDS_BYTES = 2 * TILE_ELEMS * sizeof(T);
+  static constexpr size_t TILES_BYTES = 2 * TILE_ELEMS * sizeof(T);
+  // Candidate slots after the two key tiles: [wave][slot][lane] of (score, block).
+  static constexpr size_t LDS_BYTES = TILES_BYTES + (size_t)kIdxWaves * kCandSlots * kWave * 8;
 };
 
 // An empty asm that reads every 32-bit word of x: x must be in registers
@@ -59,7 +66,7 @@ __device__ inline void hold_in_registers(const F& x) {
 }
 
 template <typename T, int DIDX, int CAP>
-__global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
+__global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     float* __restrict__ pooled, int N, int H_kv, int topk, int causal, int GT, int n_qtiles,
     int n_gtiles) {
@@ -143,8 +150,11 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
   __syncthreads();
 
   // Insert a block's pooled score into the lane's sorted list (strictly
-  // greater wins, so equal scores keep the lower block index).
-  auto insert = [&](float p, int jb) {
+  // greater wins, so equal scores keep the lower block index).  A score that
+  // does not beat the list's last entry changes nothing, so the wave skips
+  // the insertion when no lane's does.
+  auto insert = [&](float p, int jb) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(p > tv[CAP - 1]) == 0) return;
 #pragma unroll
     for (int i = CAP - 1; i >= 1; --i) {
       const bool up = p > tv[i - 1];
@@ -156,8 +166,35 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
     tv[0] = here ? p : tv[0];
     ti[0] = here ? jb : ti[0];
   };
-  // The insertion of block j-1 runs after block j's products are issued, so
-  // its arithmetic overlaps the matrix unit instead of following it.
+  // Blocks reach the list through a filter: a pooled score that beats thr,
+  // the list's last entry when the slots were last emptied, goes to the
+  // lane's next candidate slot in LDS; when some lane's slots are full, every
+  // lane inserts its candidates in the order they came.  The list only grows,
+  // so thr never exceeds its last entry and every score the list would take
+  // passes the filter; inserting in arrival order (increasing block index)
+  // keeps the tie rule.  The list therefore ends exactly as with one
+  // insertion per block, at a fraction of the vector work.
+  int2* cand = reinterpret_cast<int2*>(smem_raw + C::TILES_BYTES) + (size_t)wave * kCandSlots * kWave + lane;
+  float thr = -INFINITY;
+  int ncand = 0;
+  auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int sl = 0; sl < kCandSlots; ++sl) {
+      const int2 e = cand[sl * kWave];
+      insert(sl < ncand ? __int_as_float(e.x) : -INFINITY, e.y);
+    }
+    ncand = 0;
+    thr = tv[CAP - 1];
+  };
+  auto offer = [&](float p, int jb) __attribute__((always_inline)) {
+    if (p > thr) {
+      cand[ncand * kWave] = make_int2(__float_as_int(p), jb);
+      ++ncand;
+    }
+    if (__builtin_amdgcn_ballot_w64(ncand == kCandSlots) != 0) flush();
+  };
+  // The offer of block j-1 runs after block j's products are issued, so its
+  // arithmetic overlaps the matrix unit instead of following it.
   float p_prev = -INFINITY;
   int j_prev = -1;
   for (int j = 0; j <= jlast; ++j) {
@@ -187,7 +224,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
       }
       if (more) store_block(buf ^ 1);
       if (j_prev >= 0) {
-        insert(p_prev, j_prev);
+        offer(p_prev, j_prev);
         j_prev = -1;
       }
 #pragma unroll
@@ -222,7 +259,8 @@ __global__ __launch_bounds__(kIdxThreads) void index_topk_kernel(
     }
     __syncthreads();
   }
-  if (j_prev >= 0) insert(p_prev, j_prev);
+  if (j_prev >= 0) offer(p_prev, j_prev);
+  flush();
 
   const int tq = q0 + lane;
   if (!wave_valid || tq >= N) return;
