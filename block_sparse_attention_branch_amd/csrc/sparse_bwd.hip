@@ -100,27 +100,25 @@ __device__ inline bool decode_item(const int32_t* __restrict__ tiles, const int3
   return true;
 }
 
-// Query t and slot of item-local query qi (clamped, with a validity flag).
-__device__ inline void item_query(const Item& it, int qi, const int32_t* __restrict__ block_idx, int N, int H_kv,
-                                  int topk, int* t, int* slot, bool* valid) {
-  *valid = qi < it.nq;
-  const int qc = min(qi, it.nq - 1);
-  if (it.diag) {
-    *t = it.j * kBlock + qc;
-    const int32_t* brow = block_idx + (((size_t)it.b * N + *t) * H_kv + it.g) * topk;
-    int s = 0;
-    for (int e = 0; e < topk; ++e)
-      if (brow[e] == it.j) s = e;
-    *slot = s;
-  } else {
-    const int e = it.ent[qc];
-    *t = e >> 6;
-    *slot = e & 63;
-    if (*t < 0 || *t >= N || *slot >= topk) {
-      *valid = false;
-      *t = 0;
-      *slot = 0;
+// The item's queries, staged in LDS once per item: (t << 6) | slot, or -1
+// for an entry outside the sequence (a well-formed map never has one; it is
+// dropped rather than trusted).  The diagonal item looks up each own query's
+// slot in its selection here.
+__device__ inline void stage_item_queries(const Item& it, const int32_t* __restrict__ block_idx, int N, int H_kv,
+                                          int topk, int* qent) {
+  for (int i = threadIdx.x; i < it.nq; i += blockDim.x) {
+    int t, slot = 0;
+    if (it.diag) {
+      t = it.j * kBlock + i;
+      const int32_t* brow = block_idx + (((size_t)it.b * N + t) * H_kv + it.g) * topk;
+      for (int e = 0; e < topk; ++e)
+        if (brow[e] == it.j) slot = e;
+    } else {
+      const int e = it.ent[i];
+      t = e >> 6;
+      slot = e & 63;
     }
+    qent[i] = (t < 0 || t >= N || slot >= topk) ? -1 : ((t << 6) | slot);
   }
 }
 
@@ -137,8 +135,10 @@ __global__ __launch_bounds__(256) void idx_lse_kernel(
   constexpr int PK = DIDX + 8;
   constexpr int KSTEPS = DIDX / 16;
   __shared__ __align__(16) bf16 Ks[kBlock * PK];
+  __shared__ int qent[kLseItem > kBlock ? kLseItem : kBlock];
   Item it;
   if (!decode_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, &it)) return;
+  stage_item_queries(it, block_idx, N, H_kv, topk, qent);
   {
     const bf16* src = k_idx + ((size_t)it.b * N + (size_t)it.j * kBlock) * DIDX;
     constexpr int CPR = DIDX / 8;
@@ -151,14 +151,18 @@ __global__ __launch_bounds__(256) void idx_lse_kernel(
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // Query tiles of 32: wave w takes tiles w, w + 4, ...; a tile's query ids
-  // and q_idx rows are fetched while the previous tile computes.
+  // (from LDS) and q_idx rows are fetched while the previous tile computes.
   int tile = wave;
   if (tile * 32 >= it.nq) return;
   int t, slot;
   bool valid;
   bf16x8 qn[KSTEPS];
   auto fetch = [&](int tl) {
-    item_query(it, tl * 32 + (lane & 31), block_idx, N, H_kv, topk, &t, &slot, &valid);
+    const int qi = tl * 32 + (lane & 31);
+    const int e = qent[min(qi, it.nq - 1)];
+    valid = qi < it.nq && e >= 0;
+    t = e >= 0 ? (e >> 6) : 0;          // dropped entries are clamped for the loads
+    slot = e >= 0 ? (e & 63) : 0;
     const bf16* qrow = q_idx + (((size_t)it.b * N + t) * H_kv + it.g) * DIDX + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
