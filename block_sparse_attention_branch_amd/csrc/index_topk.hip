@@ -66,7 +66,9 @@ __device__ inline void hold_in_registers(const F& x) {
 }
 
 template <typename T, int DIDX, int CAP>
-__global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
+// A list of 63 entries (topk 64) needs the registers of a whole SIMD: one
+// workgroup per CU then, two otherwise.
+__global__ __launch_bounds__(kIdxThreads, (CAP > 31 ? 1 : 2)) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     float* __restrict__ pooled, int N, int H_kv, int topk, int causal, int GT, int n_qtiles,
     int n_gtiles) {
@@ -316,7 +318,8 @@ hipError_t launch_cap(const Problem& P, const void* q, const void* k, int32_t* b
   if (need <= 3) return launch_typed<T, DIDX, 3>(P, q, k, bi, pooled, s);
   if (need <= 7) return launch_typed<T, DIDX, 7>(P, q, k, bi, pooled, s);
   if (need <= 15) return launch_typed<T, DIDX, 15>(P, q, k, bi, pooled, s);
-  return launch_typed<T, DIDX, 31>(P, q, k, bi, pooled, s);
+  if (need <= 31) return launch_typed<T, DIDX, 31>(P, q, k, bi, pooled, s);
+  return launch_typed<T, DIDX, 63>(P, q, k, bi, pooled, s);
 }
 
 }  // namespace

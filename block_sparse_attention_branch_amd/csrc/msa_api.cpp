@@ -73,7 +73,8 @@ int check_dims(const msa_dims* d, msa::Problem* P) {
   if (d->d != 64 && d->d != 128) return fail(MSA_ERR_UNSUPPORTED, "head dim d=%d (64 or 128)", d->d);
   if (d->d_idx != 32 && d->d_idx != 64)
     return fail(MSA_ERR_UNSUPPORTED, "index dim d_idx=%d (32 or 64)", d->d_idx);
-  if (d->topk > 32) return fail(MSA_ERR_UNSUPPORTED, "topk=%d (at most 32)", d->topk);
+  // Slots live in 6 bits of the block map's entries (t << 6 | slot).
+  if (d->topk > 64) return fail(MSA_ERR_UNSUPPORTED, "topk=%d (at most 64)", d->topk);
   const int G = d->H_q / d->H_kv;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
     return fail(MSA_ERR_UNSUPPORTED, "group size H_q/H_kv=%d (1, 2, 4, 8 or 16)", G);

@@ -888,7 +888,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 // heads of one query and slot are contiguous on both sides).  D / 8 lanes per
 // row, 16 bytes each.  KM >= topk is the compile-time slot count: all partial
 // loads of the row are issued at once (slot indices past topk clamped to the
-// last slot and skipped), so a row costs one memory round trip.  Padded slots
+// last slot and skipped), so a row costs one memory round trip (two at
+// KM = 64, whose loads go in chunks of 32).  Padded slots
 // hold unwritten memory and are excluded by selection.  Row indices fit in 32
 // bits (checked by the host).
 template <int D, int KM>
@@ -906,10 +907,16 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(const bf16* __restrict__ 
   const int t = c0 + tl, g = h / G;
   const int32_t* brow = block_idx + (((size_t)b * N + t) * H_kv + g) * topk;
   const bf16* prow = part + ((size_t)bt * topk * H_q + h) * D + col;   // slot e at + e H_q D
-  bf16x8 raw[KM];
+  // Partial loads in flight: all of the row's (KM <= 32), else chunks of 32.
+  constexpr int KC = KM > 32 ? 32 : KM;
+  bf16x8 raw[KC];
+  auto load_chunk = [&](int e0) {
 #pragma unroll
-  for (int e = 0; e < KM; ++e)   // streaming loads: each partial is read once
-    raw[e] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(prow + (size_t)min(e, topk - 1) * H_q * D));
+    for (int e = 0; e < KC; ++e)   // streaming loads: each partial is read once
+      raw[e] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(prow + (size_t)min(e0 + e, topk - 1) * H_q * D));
+  };
+  load_chunk(0);
   bool ok[KM];
   if (topk == KM) {
 #pragma unroll
@@ -923,10 +930,14 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(const bf16* __restrict__ 
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < KM; ++e)
-    if (ok[e])
+  for (int e0 = 0; e0 < KM; e0 += KC) {
+    if (e0 > 0) load_chunk(e0);
 #pragma unroll
-      for (int k2 = 0; k2 < 8; ++k2) acc[k2] += (float)raw[e][k2];
+    for (int e = 0; e < KC; ++e)
+      if (ok[e0 + e])
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) acc[k2] += (float)raw[e][k2];
+  }
   bf16x8 y;
 #pragma unroll
   for (int k2 = 0; k2 < 8; ++k2) y[k2] = (bf16)acc[k2];
@@ -942,7 +953,8 @@ hipError_t launch_dq_merge(const Problem& P, const bf16* part, const int32_t* bl
   const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
   auto kern = P.topk <= 4 ? dq_merge_kernel<D, 4>
             : P.topk <= 8 ? dq_merge_kernel<D, 8>
-            : P.topk <= 16 ? dq_merge_kernel<D, 16> : dq_merge_kernel<D, 32>;
+            : P.topk <= 16 ? dq_merge_kernel<D, 16>
+            : P.topk <= 32 ? dq_merge_kernel<D, 32> : dq_merge_kernel<D, 64>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, part, block_idx, dq, P.B, P.N, P.H_kv, P.G, P.topk, c0,
                      CQ);
   return hipGetLastError();
@@ -1093,7 +1105,8 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
     if (rows_g > 0x1fffffff) return hipErrorInvalidConfiguration;
     auto mk = P.topk <= 4 ? idx_lse_merge_kernel<4>
             : P.topk <= 8 ? idx_lse_merge_kernel<8>
-            : P.topk <= 16 ? idx_lse_merge_kernel<16> : idx_lse_merge_kernel<32>;
+            : P.topk <= 16 ? idx_lse_merge_kernel<16>
+            : P.topk <= 32 ? idx_lse_merge_kernel<32> : idx_lse_merge_kernel<64>;
     hipLaunchKernelGGL(mk, dim3((unsigned)((rows_g * 4 + 255) / 256)), dim3(256), 0, s, w.idx_part, a.block_idx,
                        w.lse_idx, (int)rows_g, P.topk);
   }

@@ -333,8 +333,8 @@ __global__ __launch_bounds__((FwdCfg<T, D>::THREADS), (FwdCfg<T, D>::WAVES / 4))
 // slot count: every partial load of the row is issued up front (slot indices
 // past topk are clamped to the last slot and their weight is zero), together
 // with the row's block indices and slot log-sum-exps, so that a row costs one
-// memory round trip.  The merge: LSE = logsumexp over the valid slots and
-// o = sum_j exp(lse_j - LSE) o_j.  Padded slots (block index -1) hold
+// memory round trip (two at KM = 64, whose loads go in chunks of 32).  The
+// merge: LSE = logsumexp over the valid slots and o = sum_j exp(lse_j - LSE) o_j.  Padded slots (block index -1) hold
 // unwritten memory: they are excluded by selection, never by multiplying
 // with a zero weight.  Row indices fit in 32 bits (checked by the host).
 template <typename T, int D, int KM>
@@ -359,11 +359,16 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po
   constexpr int NS = D / 32;
   const int col = part * EPL;
   const T* prow = po + ((size_t)(bt * topk * NS + col / 32) * H_q + h) * 32 + col % 32;
-  uint4 raw[KM];
+  // Partial loads in flight: all of the row's (KM <= 32), else chunks of 32.
+  constexpr int KC = KM > 32 ? 32 : KM;
+  uint4 raw[KC];
+  auto load_chunk = [&](int e0) {
 #pragma unroll
-  for (int e = 0; e < KM; ++e)
-    raw[e] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                                           prow + (size_t)min(e, topk - 1) * NS * H_q * 32)));   // read once
+    for (int e = 0; e < KC; ++e)
+      raw[e] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                             prow + (size_t)min(e0 + e, topk - 1) * NS * H_q * 32)));   // read once
+  };
+  load_chunk(0);
   // Slot log-sum-exps in log2 units, -inf for padded slots.
   float lv[KM];
   if (topk == KM) {
@@ -396,12 +401,16 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const T* __restrict__ po
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
 #pragma unroll
-  for (int e = 0; e < KM; ++e) {
-    if (lv[e] != -INFINITY) {
-      const float wgt = __builtin_amdgcn_exp2f(lv[e] - L2);
-      const T* x = reinterpret_cast<const T*>(&raw[e]);
+  for (int e0 = 0; e0 < KM; e0 += KC) {
+    if (e0 > 0) load_chunk(e0);
 #pragma unroll
-      for (int c = 0; c < EPL; ++c) acc[c] = fmaf(wgt, to_f32(x[c]), acc[c]);
+    for (int e = 0; e < KC; ++e) {
+      if (lv[e0 + e] != -INFINITY) {
+        const float wgt = __builtin_amdgcn_exp2f(lv[e0 + e] - L2);
+        const T* x = reinterpret_cast<const T*>(&raw[e]);
+#pragma unroll
+        for (int c = 0; c < EPL; ++c) acc[c] = fmaf(wgt, to_f32(x[c]), acc[c]);
+      }
     }
   }
   const float L = L2 * kLn2;
@@ -423,7 +432,8 @@ hipError_t launch_fwd_merge(const Problem& P, const T* po, const float* pl, cons
   const unsigned blocks = (unsigned)((rows + (256 / LPR) - 1) / (256 / LPR));
   auto kern = P.topk <= 4 ? fwd_merge_kernel<T, D, 4>
             : P.topk <= 8 ? fwd_merge_kernel<T, D, 8>
-            : P.topk <= 16 ? fwd_merge_kernel<T, D, 16> : fwd_merge_kernel<T, D, 32>;
+            : P.topk <= 16 ? fwd_merge_kernel<T, D, 16>
+            : P.topk <= 32 ? fwd_merge_kernel<T, D, 32> : fwd_merge_kernel<T, D, 64>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, po, pl, block_idx, o, lse, P.B, P.N, P.H_kv, P.G,
                      P.topk, c0, CQ);
   return hipGetLastError();

@@ -40,7 +40,7 @@
  *    a workspace must be ordered on one stream.
  *  - Supported: block_size == 128, N a multiple of 128 and at most 2^22,
  *    B*N*H_q below 2^31, d in {64, 128},
- *    d_idx in {32, 64}, 1 <= topk <= 32, H_q % H_kv == 0 ([FA]
+ *    d_idx in {32, 64}, 1 <= topk <= 64, H_q % H_kv == 0 ([FA]
  *    "Architectural compatibility": GQA needs the query heads to divide into
  *    the KV heads evenly) with G = H_q / H_kv in {1, 2, 4, 8, 16}.
  *    Anything else returns MSA_ERR_UNSUPPORTED (or MSA_ERR_INVALID_ARG when it

@@ -68,7 +68,7 @@ def good_dims(**kw):
     (dict(N=1000), bnd.MSA_ERR_UNSUPPORTED),
     (dict(d=96), bnd.MSA_ERR_UNSUPPORTED),
     (dict(d_idx=48), bnd.MSA_ERR_UNSUPPORTED),
-    (dict(topk=33), bnd.MSA_ERR_UNSUPPORTED),
+    (dict(topk=65), bnd.MSA_ERR_UNSUPPORTED),
     (dict(H_q=6, H_kv=2), bnd.MSA_ERR_UNSUPPORTED),
     (dict(N=128 * (1 << 16)), bnd.MSA_ERR_UNSUPPORTED),
     (dict(B=128, N=1 << 20, H_q=16, H_kv=2), bnd.MSA_ERR_UNSUPPORTED),   # B*N*H_q = 2^31

@@ -286,6 +286,13 @@ def test_bwd_128k_planted_sampled():
     _sampled(w, "planted", 32, 104, blocks=[w.nblk - 1])
 
 
+def test_bwd_topk64_sampled():
+    # topk 64 over 72 blocks: 64-slot dQ merges and index log-sum-exps.
+    w = msa_inputs.Workload("bwd-k64", B=1, N=9216, H_q=8, H_kv=2, d=128, d_idx=64, topk=64, backward=True,
+                            seed=99)
+    _sampled(w, "normal", 48, 99, blocks=[w.nblk - 1, w.nblk - 8])
+
+
 def test_bwd_1m_sampled():
     w = msa_inputs.WORKLOADS["fwdbwd-bf16-n1m"]
     _sampled(w, "normal", 16, 5, blocks=[w.nblk - 1])

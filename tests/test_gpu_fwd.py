@@ -147,5 +147,11 @@ def test_bf16_forward_128k_planted_sampled():
     _check_sampled(msa_inputs.WORKLOADS["fwd-bf16-n128k"], "planted", 64, 104)
 
 
+def test_bf16_forward_topk64_sampled():
+    # topk 64 over 72 blocks: 64 slots per row to merge (two chunks of loads).
+    w = msa_inputs.Workload("bf16-k64", B=1, N=9216, H_q=8, H_kv=2, d=128, d_idx=64, topk=64, seed=98)
+    _check_sampled(w, "normal", 96, 98)
+
+
 def test_bf16_forward_1m_sampled():
     _check_sampled(msa_inputs.WORKLOADS["fwdbwd-bf16-n1m"], "normal", 24, 5)

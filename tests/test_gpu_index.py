@@ -108,6 +108,15 @@ def test_bf16_integer_topk_edges(topk):
     _check_full(w, "int", exact=True)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_integer_topk64_full_lists(fp8):
+    # 72 blocks: rows past block 63 keep a full list of 63 other blocks (the
+    # largest topk the library takes), earlier rows carry padding.
+    w = msa_inputs.Workload(f"int-k64-fp8{int(fp8)}", B=1, N=9216, H_q=4, H_kv=2, d=64, d_idx=64, topk=64,
+                            seed=97)
+    _check_full(w, "int", exact=True, fp8=fp8)
+
+
 def test_topk_larger_than_blocks_pads():
     w = msa_inputs.Workload("pad", B=1, N=512, H_q=1, H_kv=1, d=64, d_idx=64, topk=8, seed=5)
     x, (sel, pooled) = _run(w, "normal")
