@@ -509,8 +509,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   if (!decode_big_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, s_lo, s_hi, c0 / kBlock,
                        (c0 + CQ + kBlock - 1) / kBlock, &it))
     return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, lq = lane >> 4;            // C layout: column c, rows 4 lq + v
+  int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int c = lane & 15, lq = lane >> 4;                  // C layout: column c, rows 4 lq + v
   const int H_q = H_kv * G;
   const int b = it.b, g = it.g, j = it.j;
   const int key = 16 * wave + c;                      // this lane's key inside the block
@@ -534,12 +534,12 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     *reinterpret_cast<bf16x8*>(KIs + C::TI::off(kk, col)) =
         *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
   }
-  const int qct = wave % DT, qkp = wave / DT;         // dQ column tile and key part
+  int qct = wave % DT, qkp = wave / DT;         // dQ column tile and key part
   // The B operands of S and dP (this lane's key row of K and of V), constant
   // over the item: held in registers, which takes a third of the step's LDS
   // operand traffic off the S / dP products.
   bf16x8 kfr[KS], vfr[KS];
-  const int ict = wave % DTI, ikp = wave / DTI;       // dq_idx column tile and key part
+  int ict = wave % DTI, ikp = wave / DTI;       // dq_idx column tile and key part
 
   f32x4 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
 #pragma unroll
@@ -858,6 +858,12 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     }
     store_step(st + 1);
   }
+  // The lane's LDS offsets for the last step and the flush are recomputed
+  // past the loop rather than kept in registers through it, where the plain
+  // instances would spill them (the instances with per-score outputs spill
+  // less without this).
+  if constexpr (!EXTRA)
+    asm volatile("" : "+v"(lane), "+v"(c), "+v"(lq), "+v"(wave), "+v"(qct), "+v"(qkp), "+v"(ict), "+v"(ikp));
   dq_idx_step(n_steps - 1);   // its dz^T was completed by the loop's last barrier
   __syncthreads();            // the last step's dQ tile complete
   dq_store(n_steps - 1);
