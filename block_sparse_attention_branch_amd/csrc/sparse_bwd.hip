@@ -278,18 +278,6 @@ struct Pad {
   static constexpr int pitch = P;
   __device__ static int off(int r, int c) { return r * P + c; }
 };
-// Swz128b: rows of 128 elements (256 B, no padding) whose 16-byte chunk c of
-// row r is stored at chunk c ^ (2 (r & 7) + ((r >> 3) & 1)): transpose reads
-// of 8 consecutive rows x 2 chunks hit distinct banks.  For the K and V tiles.
-struct Swz128b {
-  static constexpr int pitch = 128;
-  __device__ static int off(int r, int c) {   // c: a multiple of 4
-    return r * 128 + (((c >> 3) ^ (2 * (r & 7) + ((r >> 3) & 1))) << 3) + (c & 7);
-  }
-};
-template <int W>
-using TileKOf = typename std::conditional<W == 128, Swz128b, Pad<W + 8>>::type;
-
 // A work item of the main kernel and the queries it covers: item-local query
 // qi < n_own is t = 128 j + qi (diagonal, causal mask); otherwise it is list
 // entry e0 + qi - n_own of block j's inverted list.
@@ -442,29 +430,37 @@ __device__ inline void head_mean16(const f32x4* p, f32x4* pb) {
 template <int D, int DIDX>
 struct Bwd16Cfg {
   using TQ = Pad<D + 16>;                  // Q, dO tiles (step rows)
-  using TK = TileKOf<D>;                   // K, V tiles (the block's keys)
   using TI = Pad<DIDX + 16>;               // q_idx, K_idx tiles
   using TS = Pad<32 + 4>;                  // dS^T, dz^T: one row of 32 step rows per key (+8 B)
-  static constexpr int PQ = TQ::pitch, PK = TK::pitch, PQI = TI::pitch, PST = TS::pitch;
+  using TT = Pad<kBlock + 16>;             // K^T, K_idx^T: one row of the 128 keys per column
+  static constexpr int PQ = TQ::pitch, PQI = TI::pitch, PST = TS::pitch, PKT = TT::pitch;
   static constexpr size_t OFF_QS = 0;                                    // Q        [32][PQ]
   static constexpr size_t OFF_DOS = OFF_QS + (size_t)32 * PQ * 2;        // dO       [32][PQ]
   static constexpr size_t OFF_QIS = OFF_DOS + (size_t)32 * PQ * 2;       // q_idx    [32][PQI]
   static constexpr size_t OFF_DST = OFF_QIS + (size_t)32 * PQI * 2;      // dS^T     [128][PST]
   static constexpr size_t OFF_DZT = OFF_DST + (size_t)kBlock * PST * 2;  // dz^T     2 x [128][PST]
   static constexpr size_t OFF_TAB = OFF_DZT + (size_t)2 * kBlock * PST * 2;   // 2 x kNumTabs x [32]
-  static constexpr size_t OFF_KS = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K  [128][PK]
-  static constexpr size_t OFF_VS = OFF_KS + (size_t)kBlock * PK * 2;     // V      [128][PK]
-  static constexpr size_t OFF_KIS = OFF_VS + (size_t)kBlock * PK * 2;    // K_idx  [128][PQI]
-  static constexpr size_t OFF_QL = OFF_KIS + (size_t)kBlock * PQI * 2;   // item queries: (t << 6) | slot
+  static constexpr size_t OFF_KT = OFF_TAB + (size_t)2 * kNumTabs * 32 * 4;   // K^T    [D][PKT]
+  static constexpr size_t OFF_KIS = OFF_KT + (size_t)D * PKT * 2;        // K_idx  [128][PQI]
+  static constexpr size_t OFF_KIT = OFF_KIS + (size_t)kBlock * PQI * 2;  // K_idx^T [DIDX][PKT]
+  static constexpr size_t OFF_QL = OFF_KIT + (size_t)DIDX * PKT * 2;     // item queries: (t << 6) | slot
   static constexpr int KPQ = kW16 / (D / 16);                             // key parts of the dQ product
   static constexpr int PDQ = D + 4;                                       // dQ tile row pitch (fp32)
   static constexpr size_t OFF_DQ = OFF_QL + (size_t)(kBlock + kBigItem) * 4;   // dQ [KPQ][32][PDQ] fp32
   static constexpr size_t LDS = OFF_DQ + (size_t)KPQ * 32 * PDQ * 4;
-  // The flush at the end of an item reuses [OFF_KS, OFF_QL) as 8 x [16][D + 4] fp32.
-  static_assert(OFF_QL - OFF_KS >= (size_t)kW16 * 16 * (D + 4) * 4, "flush scratch");
+  // The flush at the end of an item reuses [0, OFF_QL) as 8 x [16][D + 4] fp32.
+  static_assert(OFF_QL >= (size_t)kW16 * 16 * (D + 4) * 4, "flush scratch");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
-  static_assert(PQ % 8 == 0 && PQI % 8 == 0 && PST % 4 == 0, "16-byte rows for 16-byte accesses, 8-byte for dS^T");
+  static_assert(PQ % 8 == 0 && PQI % 8 == 0 && PST % 4 == 0 && PKT % 8 == 0,
+                "16-byte rows for 16-byte accesses, 8-byte for dS^T");
 };
+// Position of key kk in a row of the K^T and K_idx^T tiles.  The 16-byte
+// read at position 32 a + 8 q of a row gives lane group q the keys
+// 32 a + 4 q .. +3 and 32 a + 16 + 4 q .. +3, the K order in which the
+// transpose reads of dS^T and dz^T hand their rows to the same lanes.
+__device__ inline int kt_pos(int kk) {
+  return (kk & ~31) + 8 * ((kk >> 2) & 3) + 4 * ((kk >> 4) & 1) + (kk & 3);
+}
 
 template <int D, int DIDX, int G, bool EXTRA>
 __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
@@ -499,9 +495,9 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   bf16* dSt = reinterpret_cast<bf16*>(smem + C::OFF_DST);
   bf16* dZt2 = reinterpret_cast<bf16*>(smem + C::OFF_DZT);  // dz^T of steps of either parity
   int* tabs = reinterpret_cast<int*>(smem + C::OFF_TAB);
-  bf16* Ks = reinterpret_cast<bf16*>(smem + C::OFF_KS);
-  bf16* Vs = reinterpret_cast<bf16*>(smem + C::OFF_VS);
+  bf16* Kt = reinterpret_cast<bf16*>(smem + C::OFF_KT);
   bf16* KIs = reinterpret_cast<bf16*>(smem + C::OFF_KIS);
+  bf16* KIt = reinterpret_cast<bf16*>(smem + C::OFF_KIT);
   int* qlist = reinterpret_cast<int*>(smem + C::OFF_QL);   // (t << 6) | slot, or -1
   float* dQt = reinterpret_cast<float*>(smem + C::OFF_DQ);  // a step's dQ tile, one slice per key part
 
@@ -523,22 +519,31 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     const int t = big_query(it, qi, block_idx, N, H_kv, topk, &slot);
     qlist[qi] = t < 0 ? -1 : ((t << 6) | slot);
   }
+  // K and K_idx transposed (keys in kt_pos order) for the B operands of the
+  // dQ and dq_idx products; K_idx also row-major for the index logits.
   for (int cc = threadIdx.x; cc < kBlock * CPR; cc += kT16) {
     const int kk = cc / CPR, col = (cc % CPR) * 8;
-    const size_t row = blk_row0 + (size_t)kk * H_kv;
-    *reinterpret_cast<bf16x8*>(Ks + C::TK::off(kk, col)) = *reinterpret_cast<const bf16x8*>(k + row * D + col);
-    *reinterpret_cast<bf16x8*>(Vs + C::TK::off(kk, col)) = *reinterpret_cast<const bf16x8*>(v + row * D + col);
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(k + (blk_row0 + (size_t)kk * H_kv) * D + col);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Kt[(col + i) * C::PKT + kt_pos(kk)] = x[i];
   }
   for (int cc = threadIdx.x; cc < kBlock * CPRI; cc += kT16) {
     const int kk = cc / CPRI, col = (cc % CPRI) * 8;
-    *reinterpret_cast<bf16x8*>(KIs + C::TI::off(kk, col)) =
-        *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(k_idx + ((size_t)b * N + j * kBlock + kk) * DIDX + col);
+    *reinterpret_cast<bf16x8*>(KIs + C::TI::off(kk, col)) = x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) KIt[(col + i) * C::PKT + kt_pos(kk)] = x[i];
   }
   int qct = wave % DT, qkp = wave / DT;         // dQ column tile and key part
   // The B operands of S and dP (this lane's key row of K and of V), constant
   // over the item: held in registers, which takes a third of the step's LDS
   // operand traffic off the S / dP products.
   bf16x8 kfr[KS], vfr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {   // straight from memory: K and V rows are read only here
+    kfr[ks] = *reinterpret_cast<const bf16x8*>(k + (blk_row0 + (size_t)key * H_kv) * D + 32 * ks + 8 * lq);
+    vfr[ks] = *reinterpret_cast<const bf16x8*>(v + (blk_row0 + (size_t)key * H_kv) * D + 32 * ks + 8 * lq);
+  }
   int ict = wave % DTI, ikp = wave / DTI;       // dq_idx column tile and key part
 
   f32x4 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
@@ -549,12 +554,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   }
 #pragma unroll
   for (int i = 0; i < DTI; ++i) acc_dki[i] = zero4();
-  __syncthreads();   // item query list and the K, V, K_idx tiles ready
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kfr[ks] = *reinterpret_cast<const bf16x8*>(Ks + C::TK::off(key, 32 * ks + 8 * lq));
-    vfr[ks] = *reinterpret_cast<const bf16x8*>(Vs + C::TK::off(key, 32 * ks + 8 * lq));
-  }
+  __syncthreads();   // item query list and the K^T, K_idx, K_idx^T tiles ready
 
   // Per-thread share of a step, loaded one step ahead: one 16-byte chunk of
   // Q and of dO (thread < 32 CPR) with the row's statistics when the chunk is
@@ -667,7 +667,9 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
       for (int ks = 0; ks < 4 / KPI; ++ks) {
         const int k0 = 32 * (ikp * (4 / KPI) + ks) + 4 * lq;
         o[t] = mma16(tr16<typename C::TS>(dZt, 16 * t, k0, k0 + 16, lane),
-                     tr16<typename C::TI>(KIs, 16 * ict, k0, k0 + 16, lane), o[t]);
+                     *reinterpret_cast<const bf16x8*>(KIt + (16 * ict + c) * C::PKT + 32 * (ikp * (4 / KPI) + ks) +
+                                                      8 * lq),
+                     o[t]);
       }
     }
 #pragma unroll
@@ -833,10 +835,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
       // compiler read K again for the second tile).
       bf16x8 kq[4 / KPQ];
 #pragma unroll
-      for (int ks = 0; ks < 4 / KPQ; ++ks) {
-        const int k0 = 32 * (qkp * (4 / KPQ) + ks) + 4 * lq;   // keys k0 .. k0+3, k0+16 .. k0+19
-        kq[ks] = tr16<typename C::TK>(Ks, 16 * qct, k0, k0 + 16, lane);
-      }
+      for (int ks = 0; ks < 4 / KPQ; ++ks)   // keys k0 .. k0+3, k0+16 .. k0+19 of the dS^T reads below
+        kq[ks] = *reinterpret_cast<const bf16x8*>(Kt + (16 * qct + c) * C::PKT + 32 * (qkp * (4 / KPQ) + ks) + 8 * lq);
       f32x4 o[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -870,7 +870,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 
   // Flush the wave's dK, dV (group g) and dk_idx (shared by the groups):
   // C layout [d rows][16 keys] -> LDS [16 keys][d] -> atomics of whole key rows.
-  float* scr = reinterpret_cast<float*>(smem + C::OFF_KS) + wave * 16 * (D + 4);
+  float* scr = reinterpret_cast<float*>(smem) + wave * 16 * (D + 4);
   auto flush = [&](const f32x4* acc, int ntile, int width, float* dst_row0, size_t row_stride) {
     __syncthreads();
     for (int dt = 0; dt < ntile; ++dt)
