@@ -127,7 +127,7 @@ __device__ inline void stage_item_queries(const Item& it, const int32_t* __restr
 // partials (max, sum) per slot, then a merge.
 // ---------------------------------------------------------------------------
 template <int DIDX>
-__global__ __launch_bounds__(256) void idx_lse_kernel(
+__global__ __launch_bounds__(256, 4) void idx_lse_kernel(
     const bf16* __restrict__ q_idx, const bf16* __restrict__ k_idx, const int32_t* __restrict__ block_idx,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ offs, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ tiles, float2* __restrict__ part, int N, int H_kv, int topk, int causal,
@@ -179,31 +179,54 @@ __global__ __launch_bounds__(256) void idx_lse_kernel(
     const int next = tile + 4;
     const bool more = next * 32 < it.nq;
     if (more) fetch(next);
-    f32x16 s[4];
+    // The block's 128 keys in two halves of 64 (32 accumulator registers at a
+    // time), combined as an online log-sum-exp.  Only the diagonal item
+    // masks (keys after the query); the scale c > 0 goes inside the
+    // exponent: max(c s) = c max(s).
+    float m = -INFINITY, l = 0.f;
+#pragma unroll 1
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 s[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      s[mt] = zero16();
-      const bf16* kp = Ks + (mt * 32 + (lane & 31)) * PK + 8 * (lane >> 5);
+      for (int h = 0; h < 2; ++h) {
+        const int mt = 2 * hf + h;
+        s[h] = zero16();
+        const bf16* kp = Ks + (mt * 32 + (lane & 31)) * PK + 8 * (lane >> 5);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + ks * 16), qf[ks],
-                                                         s[mt], 0, 0, 0);
-    }
-    float m = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const bool vis = !(it.diag && causal && it.j * kBlock + mt * 32 + c_row(v, lane) > tc);
-        s[mt][v] = vis ? s[mt][v] * c : -INFINITY;
-        m = fmaxf(m, s[mt][v]);
+        for (int ks = 0; ks < KSTEPS; ++ks)
+          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + ks * 16), qf[ks],
+                                                         s[h], 0, 0, 0);
       }
-    m = fmaxf(m, swap_half(m));
-    float l = 0.f;
+      if (it.diag && causal) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) l += __builtin_amdgcn_exp2f(s[mt][v] - m);
+          for (int v = 0; v < 16; ++v)
+            if (it.j * kBlock + (2 * hf + h) * 32 + c_row(v, lane) > tc) s[h][v] = -INFINITY;
+      }
+      float mh = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mh = fmaxf(mh, s[h][v]);
+      mh = fmaxf(mh, swap_half(mh)) * c;       // the same in both lanes of the query
+      const float off = mh == -INFINITY ? 0.f : mh;   // a fully masked half adds 0
+      float lh = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) lh += __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][v], c, -off));
+      if (hf == 0) {
+        m = mh;
+        l = lh;
+      } else {
+        // Finite: half 0 holds key 128 j <= t, or is unmasked.  A masked half
+        // (mh = -inf) contributes exp2(-inf) * 0 = 0.
+        const float mn = fmaxf(m, mh);
+        l = l * __builtin_amdgcn_exp2f(m - mn) + lh * __builtin_amdgcn_exp2f(mh - mn);
+        m = mn;
+      }
+    }
     l += swap_half(l);
     if (vc && lane < 32) part[(((size_t)it.b * N + tc) * H_kv + it.g) * topk + sc] = make_float2(m, l);
     if (!more) break;
@@ -512,7 +535,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   const int key = 16 * wave + c;                      // this lane's key inside the block
   const int u = j * kBlock + key;
   const size_t blk_row0 = ((size_t)b * N + (size_t)j * kBlock) * H_kv + g;   // key 0 of the block
-  const int nq = it.n_own + it.ne;
+  const int nq = it.n_own + it.ne;   // >= 1: an item holds its diagonal queries or list entries
 
   for (int qi = threadIdx.x; qi < nq; qi += kT16) {
     int slot;
