@@ -17,7 +17,8 @@
 //   rows [N * topk]          entries (t << 6) | slot, slot = position of j in
 //                            block_idx[b, t, g, :] (at most topk - 1 per query
 //                            for a well-formed row; room for topk keeps a
-//                            malformed row in bounds)
+//                            malformed row in bounds); one spare entry follows
+//                            the last region, the target of dropped stores
 // Built by count -> column scan -> row scan -> ordered scatter.  Every step is
 // deterministic: the scatter walks each super-block's queries in order.
 #include "msa_internal.h"
@@ -63,20 +64,36 @@ __global__ __launch_bounds__(256) void bm_count_kernel(const int32_t* __restrict
 }
 
 // Exclusive scan of every column over super-blocks; row nsb gets the totals.
-__global__ __launch_bounds__(256) void bm_scan_cols_kernel(int32_t* __restrict__ pos, int nblk, int nsb,
-                                                           int n_bg) {
-  const int cols_per_bg = (nblk + 255) / 256;
-  const int bg = blockIdx.x / cols_per_bg;
-  const int j = (blockIdx.x % cols_per_bg) * 256 + threadIdx.x;
-  if (bg >= n_bg || j >= nblk) return;
+// A workgroup takes 64 columns of one (b, g): each of its 16 waves sums a run
+// of rows (64 columns = 256 contiguous bytes per row), the run totals are
+// scanned in LDS, and each wave rewrites its run.
+constexpr int kScanSegs = 16;
+__global__ __launch_bounds__(64 * kScanSegs) void bm_scan_cols_kernel(int32_t* __restrict__ pos, int nblk,
+                                                                      int nsb) {
+  __shared__ int32_t seg_tot[kScanSegs][64];
+  const int cpb = (nblk + 63) / 64;
+  const int bg = blockIdx.x / cpb;
+  const int c = threadIdx.x & 63, seg = threadIdx.x >> 6;
+  const int j = (blockIdx.x % cpb) * 64 + c;
+  const int per = (nsb + kScanSegs - 1) / kScanSegs;
+  const int s0 = min(seg * per, nsb), s1 = min(s0 + per, nsb);
+  const bool ok = j < nblk;
   int32_t* base = pos + (size_t)bg * (nsb + 1) * nblk + j;
+  int32_t sum = 0;
+  if (ok)
+    for (int s = s0; s < s1; ++s) sum += base[(size_t)s * nblk];
+  seg_tot[seg][c] = sum;
+  __syncthreads();
   int32_t run = 0;
-  for (int s = 0; s < nsb; ++s) {
-    const int32_t c = base[(size_t)s * nblk];
-    base[(size_t)s * nblk] = run;
-    run += c;
+  for (int k = 0; k < seg; ++k) run += seg_tot[k][c];
+  if (ok) {
+    for (int s = s0; s < s1; ++s) {
+      const int32_t v = base[(size_t)s * nblk];
+      base[(size_t)s * nblk] = run;
+      run += v;
+    }
+    if (seg == kScanSegs - 1) base[(size_t)nsb * nblk] = run;   // the list lengths
   }
-  base[(size_t)nsb * nblk] = run;
 }
 
 // Block-wide exclusive scan of `in[0..n)` into `out[0..n]` (out[n] = total),
@@ -114,8 +131,13 @@ __global__ __launch_bounds__(1024) void bm_offsets_kernel(const int32_t* __restr
 }
 
 // Ordered scatter: one wave per (b, g, super-block) walks its queries in
-// increasing t; lane e handles entry e of the query's row.  The entries of a
-// row name distinct blocks, so the LDS cursors never collide within a step.
+// increasing t, QW = 64 / TP of them per pass (TP = topk rounded up to a
+// power of two); lane q TP + e handles entry e of the pass's query q.  The
+// pass's rows are loaded together; then the queries take their cursors in
+// order, q = 0 first.  The entries of one row name distinct blocks, so the
+// lanes of one query never share a cursor, and a single wave's LDS accesses
+// complete in program order, so query q sees the cursors that queries < q
+// advanced.
 __global__ __launch_bounds__(64) void bm_scatter_kernel(const int32_t* __restrict__ block_idx,
                                                         const int32_t* __restrict__ pos,
                                                         const int32_t* __restrict__ offs,
@@ -131,22 +153,36 @@ __global__ __launch_bounds__(64) void bm_scatter_kernel(const int32_t* __restric
   __syncthreads();
   const int cap = N * topk;   // per (b, g): a row holds at most topk entries
   int32_t* out = rows + (size_t)bg * cap;
+  int32_t* spare = rows + (size_t)(gridDim.x / nsb) * cap;
   const int t0 = s * SB * kBlock;
   const int t1 = min(t0 + SB * kBlock, N);
-  const int e = threadIdx.x;
-  const bool active = e < topk;
-  const int32_t* src = block_idx + (((size_t)b * N) * H_kv + g) * topk + e;
+  int TP = 1;
+  while (TP < topk) TP *= 2;
+  const int QW = 64 / TP;                      // queries per pass (TP <= 64)
+  const int q = threadIdx.x / TP, e = threadIdx.x % TP;
+  const bool lane_on = e < topk;
+  // Unconditional loads at clamped, in-bounds addresses (t0 < t1 for every
+  // super-block), so the next pass's rows stay in flight through this pass;
+  // lanes and queries out of range are dropped when the value is used.
+  const int32_t* src = block_idx + (((size_t)b * N) * H_kv + g) * topk + min(e, topk - 1);
   const size_t tstride = (size_t)H_kv * topk;
-  int j_next = (active && t0 < t1) ? src[(size_t)t0 * tstride] : -1;
-  for (int t = t0; t < t1; ++t) {
-    const int j = j_next;
-    j_next = (active && t + 1 < t1) ? src[(size_t)(t + 1) * tstride] : -1;
-    if ((unsigned)j < (unsigned)nblk && j != t / kBlock) {
-      const int32_t p = cursor[j];
-      cursor[j] = p + 1;
-      if ((unsigned)p < (unsigned)cap) out[p] = (t << 6) | e;
+  auto load = [&](int tb) { return src[(size_t)min(tb + q, t1 - 1) * tstride]; };
+  int j_next = load(t0);
+  for (int tb = t0; tb < t1; tb += QW) {
+    const int t = tb + q;
+    const int j = (lane_on && t < t1) ? j_next : -1;
+    j_next = load(tb + QW);
+    const bool on = (unsigned)j < (unsigned)nblk && j != t / kBlock;
+    int p = -1;
+    for (int qq = 0; qq < QW; ++qq) {
+      if (on && q == qq) {
+        p = cursor[j];
+        cursor[j] = p + 1;
+      }
     }
-    __syncthreads();
+    // Unconditional store (dropped lanes write the spare entry), so that the
+    // wait for the next pass's rows need not wait for it.
+    *(on && (unsigned)p < (unsigned)cap ? out + p : spare) = (t << 6) | e;
   }
 }
 
@@ -160,7 +196,7 @@ size_t block_map_bytes(const Problem& P) {
   const size_t bg = (size_t)P.B * P.H_kv;
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   return al(bg * (nsb + 1) * P.nblk * 4) + al(bg * (P.nblk + 1) * 4) +
-         al(bg * (size_t)P.N * P.topk * 4) + al((bg * P.nblk + 1) * 4) + al(64 * 4);
+         al((bg * (size_t)P.N * P.topk + 1) * 4) + al((bg * P.nblk + 1) * 4) + al(64 * 4);
 }
 
 void block_map_carve(const Problem& P, void* ws, BlockMap* m) {
@@ -174,7 +210,7 @@ void block_map_carve(const Problem& P, void* ws, BlockMap* m) {
   m->offs = reinterpret_cast<int32_t*>(p);
   p += al(bg * (P.nblk + 1) * 4);
   m->rows = reinterpret_cast<int32_t*>(p);
-  p += al(bg * (size_t)P.N * P.topk * 4);
+  p += al((bg * (size_t)P.N * P.topk + 1) * 4);   // + the spare entry
   m->tiles = reinterpret_cast<int32_t*>(p);
   p += al((bg * P.nblk + 1) * 4);
   m->counters = reinterpret_cast<int32_t*>(p);
@@ -200,9 +236,9 @@ hipError_t launch_block_map(const Problem& P, const int32_t* block_idx, const Bl
   hipLaunchKernelGGL(bm_count_kernel, dim3(n_bg * m.nsb), dim3(256), lds, s, block_idx, m.pos, P.N,
                      P.H_kv, P.topk, P.nblk, m.nsb, m.SB);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int cols_per_bg = (P.nblk + 255) / 256;
-  hipLaunchKernelGGL(bm_scan_cols_kernel, dim3(n_bg * cols_per_bg), dim3(256), 0, s, m.pos, P.nblk,
-                     m.nsb, n_bg);
+  const int cols_per_bg = (P.nblk + 63) / 64;
+  hipLaunchKernelGGL(bm_scan_cols_kernel, dim3(n_bg * cols_per_bg), dim3(64 * kScanSegs), 0, s, m.pos, P.nblk,
+                     m.nsb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bm_offsets_kernel, dim3(n_bg), dim3(1024), 0, s, m.pos, m.offs, P.nblk, m.nsb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
