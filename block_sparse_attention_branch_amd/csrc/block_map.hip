@@ -133,11 +133,13 @@ __global__ __launch_bounds__(1024) void bm_offsets_kernel(const int32_t* __restr
 // Ordered scatter: one wave per (b, g, super-block) walks its queries in
 // increasing t, QW = 64 / TP of them per pass (TP = topk rounded up to a
 // power of two); lane q TP + e handles entry e of the pass's query q.  The
-// pass's rows are loaded together; then the queries take their cursors in
-// order, q = 0 first.  The entries of one row name distinct blocks, so the
-// lanes of one query never share a cursor, and a single wave's LDS accesses
-// complete in program order, so query q sees the cursors that queries < q
-// advanced.
+// passes go in batches of kBatch: the batch's rows are loaded first (all in
+// flight together), then the queries take their list cursors in order, q = 0
+// first within a pass, and the batch's entries are stored last.  The entries
+// of one row name distinct blocks, so the lanes of one query never share a
+// cursor, and a single wave's LDS accesses complete in program order, so each
+// query sees the cursors that the queries before it advanced.
+constexpr int kBatch = 16;
 __global__ __launch_bounds__(64) void bm_scatter_kernel(const int32_t* __restrict__ block_idx,
                                                         const int32_t* __restrict__ pos,
                                                         const int32_t* __restrict__ offs,
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(64) void bm_scatter_kernel(const int32_t* __restric
   __syncthreads();
   const int cap = N * topk;   // per (b, g): a row holds at most topk entries
   int32_t* out = rows + (size_t)bg * cap;
-  int32_t* spare = rows + (size_t)(gridDim.x / nsb) * cap;
+  int32_t* spare = rows + (size_t)(gridDim.x / nsb) * cap;   // one past the last region
   const int t0 = s * SB * kBlock;
   const int t1 = min(t0 + SB * kBlock, N);
   int TP = 1;
@@ -161,28 +163,33 @@ __global__ __launch_bounds__(64) void bm_scatter_kernel(const int32_t* __restric
   const int QW = 64 / TP;                      // queries per pass (TP <= 64)
   const int q = threadIdx.x / TP, e = threadIdx.x % TP;
   const bool lane_on = e < topk;
-  // Unconditional loads at clamped, in-bounds addresses (t0 < t1 for every
-  // super-block), so the next pass's rows stay in flight through this pass;
+  // Loads at clamped, in-bounds addresses (t0 < t1 for every super-block);
   // lanes and queries out of range are dropped when the value is used.
   const int32_t* src = block_idx + (((size_t)b * N) * H_kv + g) * topk + min(e, topk - 1);
   const size_t tstride = (size_t)H_kv * topk;
-  auto load = [&](int tb) { return src[(size_t)min(tb + q, t1 - 1) * tstride]; };
-  int j_next = load(t0);
-  for (int tb = t0; tb < t1; tb += QW) {
-    const int t = tb + q;
-    const int j = (lane_on && t < t1) ? j_next : -1;
-    j_next = load(tb + QW);
-    const bool on = (unsigned)j < (unsigned)nblk && j != t / kBlock;
-    int p = -1;
-    for (int qq = 0; qq < QW; ++qq) {
-      if (on && q == qq) {
-        p = cursor[j];
-        cursor[j] = p + 1;
+  for (int tb0 = t0; tb0 < t1; tb0 += kBatch * QW) {
+    int jr[kBatch], pr[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) jr[k] = src[(size_t)min(tb0 + k * QW + q, t1 - 1) * tstride];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int t = tb0 + k * QW + q;
+      const int j = (lane_on && t < t1) ? jr[k] : -1;
+      const bool on = (unsigned)j < (unsigned)nblk && j != t / kBlock;
+      int p = -1;
+      for (int qq = 0; qq < QW; ++qq) {
+        if (on && q == qq) {
+          p = cursor[j];
+          cursor[j] = p + 1;
+        }
       }
+      pr[k] = on && (unsigned)p < (unsigned)cap ? p : -1;
     }
-    // Unconditional store (dropped lanes write the spare entry), so that the
-    // wait for the next pass's rows need not wait for it.
-    *(on && (unsigned)p < (unsigned)cap ? out + p : spare) = (t << 6) | e;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int t = tb0 + k * QW + q;
+      *(pr[k] >= 0 ? out + pr[k] : spare) = (t << 6) | e;   // dropped lanes write the spare entry
+    }
   }
 }
 
