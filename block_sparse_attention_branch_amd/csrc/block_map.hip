@@ -146,12 +146,35 @@ __global__ __launch_bounds__(64) void bm_scatter_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ rows, int N, int H_kv,
                                                         int topk, int nblk, int nsb, int SB) {
   extern __shared__ int32_t cursor[];
-  const int s = blockIdx.x % nsb;
-  const int bg = blockIdx.x / nsb;
+  // Workgroup w runs on XCD w mod 8.  When nsb is a multiple of 8, XCD x
+  // takes the x-th eighth of every (b, g)'s super-blocks, in order, so the
+  // entries that neighbouring super-blocks append to one list (adjacent in
+  // memory) meet in one L2 instead of leaving eight as partial lines.
+  int s, bg;
+  if (nsb % 8 == 0) {
+    const int per = nsb / 8, k = blockIdx.x / 8;
+    bg = k / per;
+    s = (blockIdx.x % 8) * per + k % per;
+  } else {
+    s = blockIdx.x % nsb;
+    bg = blockIdx.x / nsb;
+  }
   const int b = bg / H_kv, g = bg % H_kv;
   const int32_t* prow = pos + ((size_t)bg * (nsb + 1) + s) * nblk;
   const int32_t* orow = offs + (size_t)bg * (nblk + 1);
-  for (int j = threadIdx.x; j < nblk; j += blockDim.x) cursor[j] = orow[j] + prow[j];
+  // Cursors: 8 columns per lane per round, all loads in flight together.
+  for (int j0 = threadIdx.x; j0 < nblk; j0 += 8 * 64) {
+    int32_t o[8], c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int jc = min(j0 + 64 * k, nblk - 1);
+      o[k] = orow[jc];
+      c[k] = prow[jc];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (j0 + 64 * k < nblk) cursor[j0 + 64 * k] = o[k] + c[k];
+  }
   __syncthreads();
   const int cap = N * topk;   // per (b, g): a row holds at most topk entries
   int32_t* out = rows + (size_t)bg * cap;
