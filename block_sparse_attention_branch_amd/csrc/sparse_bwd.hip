@@ -508,7 +508,6 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   constexpr int NT = kNumTabs * 32;
   // dQ: column tile w % DT over the key part w / DT (of KPQ parts); dq_idx likewise.
   constexpr int KPQ = kW16 / DT;    // 1 (d = 128) or 2 (d = 64) parts of the 128 keys
-  constexpr int KPI = kW16 / DTI;   // 2 (d_idx = 64) or 4 (d_idx = 32)
   static_assert(kW16 % DT == 0 && kW16 % DTI == 0, "wave split");
   static_assert(32 * CPR <= kT16 && 32 * CPRI <= kT16, "one tile chunk per thread");
   extern __shared__ __align__(16) char smem[];
@@ -567,7 +566,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     kfr[ks] = *reinterpret_cast<const bf16x8*>(k + (blk_row0 + (size_t)key * H_kv) * D + 32 * ks + 8 * lq);
     vfr[ks] = *reinterpret_cast<const bf16x8*>(v + (blk_row0 + (size_t)key * H_kv) * D + 32 * ks + 8 * lq);
   }
-  int ict = wave % DTI, ikp = wave / DTI;       // dq_idx column tile and key part
+  int ict = wave % DTI, ikp = wave / DTI;       // dq_idx column tile; ikp = 0: the wave that computes it
 
   f32x4 acc_dv[DT], acc_dk[DT], acc_dki[DTI];
 #pragma unroll
@@ -674,12 +673,17 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   const float c_s = scale * kLog2e;
   const float c_i = scale_idx * kLog2e;
   const int n_steps = (nq * G + 31) / 32;
-  // dq_idx[query rows, column tile ict] = dz K_idx over key part ikp, for
+  // dq_idx[query rows, column tile ict] = dz K_idx over the block's keys, for
   // step st.  It runs at the top of step st + 1, before that step's loads are
   // issued: its atomics are conditional, so the compiler cannot count them, and
   // there they sit behind no load that has to be waited for (dz^T is double
   // buffered for it).
   auto dq_idx_step = [&](int st) {
+    // The waves of key part 0 take all 128 keys of their column tile and the
+    // others skip, so each dq_idx value gets one atomic per step rather than
+    // one per key part (at d_idx = 64 a skipping wave shares its SIMD with a
+    // working one).
+    if (ikp != 0) return;
     const int* tb = tabs + (st & 1) * NT;
     const bf16* dZt = dZt2 + (st & 1) * kBlock * C::PST;
     f32x4 o[NTQ];
@@ -687,12 +691,10 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     for (int t = 0; t < NTQ; ++t) {
       o[t] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < 4 / KPI; ++ks) {
-        const int k0 = 32 * (ikp * (4 / KPI) + ks) + 4 * lq;
+      for (int ks = 0; ks < 4; ++ks) {
+        const int k0 = 32 * ks + 4 * lq;
         o[t] = mma16(tr16<typename C::TS>(dZt, 16 * t, k0, k0 + 16, lane),
-                     *reinterpret_cast<const bf16x8*>(KIt + (16 * ict + c) * C::PKT + 32 * (ikp * (4 / KPI) + ks) +
-                                                      8 * lq),
-                     o[t]);
+                     *reinterpret_cast<const bf16x8*>(KIt + (16 * ict + c) * C::PKT + 32 * ks + 8 * lq), o[t]);
       }
     }
 #pragma unroll
