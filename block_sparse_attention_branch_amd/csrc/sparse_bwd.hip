@@ -274,10 +274,11 @@ __global__ __launch_bounds__(256) void idx_lse_merge_kernel(const float2* __rest
 // Main fused backward: work items, step tables and LDS tile layouts.
 // ---------------------------------------------------------------------------
 // Work items of the main kernel: the queries of KV block j (its own 128, with
-// the causal mask) together with the first kBigItem entries of its inverted
-// list, or a later run of kBigItem list entries.  Long items keep the
-// per-item flush of dK, dV and dk_idx rare.
-constexpr int kBigItem = 1024;
+// the causal mask) together with the first item_q entries of its inverted
+// list, or a later run of item_q list entries.  Long items keep the per-item
+// flush of dK, dV and dk_idx rare; item_q (at most kBigItem) is chosen per
+// launch so that the items still outnumber the CUs many times over.
+constexpr int kBigItem = 4096;
 
 // Per-step tables (32 entries each) in LDS, double buffered.
 enum : int {
@@ -312,7 +313,7 @@ struct BigItem {
 __device__ inline bool decode_big_item(const int32_t* __restrict__ tiles, const int32_t* __restrict__ pos,
                                        const int32_t* __restrict__ offs, const int32_t* __restrict__ rows,
                                        int n_lists, int N, int H_kv, int topk, int nblk, int nsb, int s_lo,
-                                       int s_hi, int jb_lo, int jb_hi, BigItem* it) {
+                                       int s_hi, int jb_lo, int jb_hi, int item_q, BigItem* it) {
   const int w = xcd_item(tiles[n_lists]);
   if (w < 0) return false;
   int lo = 0, hi = n_lists - 1;
@@ -330,8 +331,8 @@ __device__ inline bool decode_big_item(const int32_t* __restrict__ tiles, const 
   const int seg0 = pb[(size_t)s_lo * nblk], seg1 = pb[(size_t)s_hi * nblk];
   const bool diag = it->j >= jb_lo && it->j < jb_hi;
   it->n_own = (li == 0 && diag) ? kBlock : 0;
-  it->e0 = seg0 + li * kBigItem;
-  it->ne = max(0, min(kBigItem, seg1 - it->e0));
+  it->e0 = seg0 + li * item_q;
+  it->ne = max(0, min(item_q, seg1 - it->e0));
   it->ent = rows + (size_t)bg * N * topk + offs[(size_t)bg * (nblk + 1) + it->j];
   return true;
 }
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     float* __restrict__ dk_acc, float* __restrict__ dv_acc, float* __restrict__ dq_idx,
     float* __restrict__ dk_idx, float* __restrict__ dscore, float* __restrict__ kl, int N, int H_kv, int topk,
     int causal, int nblk, int nsb, int n_lists, float scale, float scale_idx, float lam, int n_prow,
-    int n_grows, int c0, int CQ, int s_lo, int s_hi) {
+    int n_grows, int c0, int CQ, int s_lo, int s_hi, int item_q) {
   using C = Bwd16Cfg<D, DIDX>;
   constexpr int KS = D / 32;        // 32-wide k-steps over d
   constexpr int KSI = DIDX / 32;    // 32-wide k-steps over d_idx
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 
   BigItem it;
   if (!decode_big_item(tiles, pos, offs, rows, n_lists, N, H_kv, topk, nblk, nsb, s_lo, s_hi, c0 / kBlock,
-                       (c0 + CQ + kBlock - 1) / kBlock, &it))
+                       (c0 + CQ + kBlock - 1) / kBlock, item_q, &it))
     return;
   int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int c = lane & 15, lq = lane >> 4;                  // C layout: column c, rows 4 lq + v
@@ -1012,7 +1013,7 @@ hipError_t to_bf16(const float* src, void* dst, size_t n, hipStream_t s) {
 
 template <int D, int DIDX, int G>
 hipError_t run_main(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w, int grid,
-                    int c0, int CQ, int s_lo, int s_hi, hipStream_t s) {
+                    int c0, int CQ, int s_lo, int s_hi, int item_q, hipStream_t s) {
   using C = Bwd16Cfg<D, DIDX>;
   // The optional per-score outputs get their own instantiation so that the
   // plain training path carries none of their registers.
@@ -1027,24 +1028,39 @@ hipError_t run_main(const Problem& P, const BwdArgs& a, const BlockMap& m, const
                      a.block_idx, m.pos, m.offs, m.rows, m.tiles, w.dq_part, w.dk_acc, w.dv_acc, a.dq_idx,
                      a.dk_idx, a.dscore, a.kl, P.N, P.H_kv, P.topk, P.causal, P.nblk, m.nsb,
                      P.B * P.H_kv * P.nblk, P.scale, P.scale_idx, a.kl_weight, P.B * CQ * P.H_q * P.topk,
-                     P.B * P.N * P.H_kv, c0, CQ, s_lo, s_hi);
+                     P.B * P.N * P.H_kv, c0, CQ, s_lo, s_hi, item_q);
   return hipGetLastError();
 }
 
 template <int D, int DIDX>
 hipError_t run_main_g(const Problem& P, const BwdArgs& a, const BlockMap& m, const BwdScratch& w, int grid, int c0,
-                      int CQ, int s_lo, int s_hi, hipStream_t s) {
+                      int CQ, int s_lo, int s_hi, int item_q, hipStream_t s) {
   switch (P.G) {
-    case 1: return run_main<D, DIDX, 1>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
-    case 2: return run_main<D, DIDX, 2>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
-    case 4: return run_main<D, DIDX, 4>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
-    case 8: return run_main<D, DIDX, 8>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
-    case 16: return run_main<D, DIDX, 16>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, s);
+    case 1: return run_main<D, DIDX, 1>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, item_q, s);
+    case 2: return run_main<D, DIDX, 2>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, item_q, s);
+    case 4: return run_main<D, DIDX, 4>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, item_q, s);
+    case 8: return run_main<D, DIDX, 8>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, item_q, s);
+    case 16: return run_main<D, DIDX, 16>(P, a, m, w, grid, c0, CQ, s_lo, s_hi, item_q, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+// List entries per backward work item for a query chunk of CQ queries: the
+// largest of 4096, 2048, 1024 that still gives at least 24 items per CU for
+// lists of the average length (a chunk's lists hold about (topk - 1) entries
+// per query and group).  Longer items flush dK, dV and dk_idx less often;
+// enough of them keep the CUs evenly loaded (measured: 4096 is 1% faster at
+// N = 128K, and 9% slower than 1024 at B = 4, N = 8K, where it leaves 8
+// items per CU).
+static int bwd_item_queries(const Problem& P, int CQ) {
+  const double lists = (double)P.B * P.H_kv * P.nblk;
+  const double avg_len = (double)P.B * P.H_kv * CQ * (P.topk - 1) / lists;
+  for (int q = kBigItem; q > 1024; q /= 2)
+    if (lists * std::ceil(avg_len / q) >= 24.0 * 256) return q;
+  return 1024;
+}
 
 int bwd_chunk_queries(const Problem& P) {
   // Queries per chunk of the main kernel: their dQ partials (bf16, one row per
@@ -1143,25 +1159,26 @@ hipError_t launch_sparse_bwd(const Problem& P, const BwdArgs& a, const BlockMap&
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // Main kernel per query chunk (long items: own queries + up to kBigItem
+  // Main kernel per query chunk (long items: own queries + up to item_q
   // list entries), then the chunk's dq from its partials.
   const int chunk = bwd_chunk_queries(P);
   const int span = block_map_super_span(P);
   for (int c0 = 0; c0 < P.N; c0 += chunk) {
     const int c1 = c0 + chunk < P.N ? c0 + chunk : P.N;
     const int CQ = c1 - c0;
-    if ((e = launch_block_items(P, m, c0, c1, kBigItem, s, 1)) != hipSuccess) return e;
-    size_t g2 = block_items_upper_bound(P, c0, c1, kBigItem);
+    const int item_q = bwd_item_queries(P, CQ);
+    if ((e = launch_block_items(P, m, c0, c1, item_q, s, 1)) != hipSuccess) return e;
+    size_t g2 = block_items_upper_bound(P, c0, c1, item_q);
     g2 = (g2 + 7) & ~size_t(7);
     if (g2 > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int s_lo = c0 / span;
     const int s_hi = (c1 == P.N) ? m.nsb : c1 / span;
     {
       ProfScope prof("bwd_main", s);
-      if (P.d == 128 && P.d_idx == 64) e = run_main_g<128, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
-      else if (P.d == 128) e = run_main_g<128, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
-      else if (P.d_idx == 64) e = run_main_g<64, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
-      else e = run_main_g<64, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, s);
+      if (P.d == 128 && P.d_idx == 64) e = run_main_g<128, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, item_q, s);
+      else if (P.d == 128) e = run_main_g<128, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, item_q, s);
+      else if (P.d_idx == 64) e = run_main_g<64, 64>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, item_q, s);
+      else e = run_main_g<64, 32>(P, a, m, w, (int)g2, c0, CQ, s_lo, s_hi, item_q, s);
       if (e != hipSuccess) return e;
     }
     {
