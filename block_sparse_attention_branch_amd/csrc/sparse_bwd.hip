@@ -21,7 +21,8 @@
 //                        the index logits over the block (KV-outer, MFMA)
 //   idx_lse_merge_kernel lse_idx[b,t,g] over the selected support
 //   bwd_main16_kernel    per query chunk and work item (KV block j of group g,
-//                        its own queries and up to 1024 list entries): 8 waves
+//                        its own queries and up to 1024-4096 list entries,
+//                        chosen per launch): 8 waves
 //                        of 16 keys keep dK, dV, dk_idx in registers; per 32
 //                        (query, head) rows they rebuild S and P, dP, dS, the
 //                        index logits, p_px, the head-averaged teacher pbar and
