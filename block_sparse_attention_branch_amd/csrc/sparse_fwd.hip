@@ -15,7 +15,7 @@
 //
 // Structure (two kernels per query chunk):
 //   1. sparse_fwd_kernel: one workgroup per work item = (b, g, KV block j,
-//      up to 384 queries that selected j, or its own 128).  K_j and V_j^T are staged in LDS
+//      up to 768 queries that selected j, or its own 128).  K_j and V_j^T are staged in LDS
 //      once; each wave takes 32 (query, head) rows at a time:
 //        S^T = K_j Q^T      (32x32 MFMA: keys are tile rows, a lane holds
 //                            one (query, head) row and 16 keys per tile)
@@ -33,7 +33,7 @@ namespace msa {
 namespace {
 
 
-constexpr int kItemQueries = 384;     // list entries per work item (the diagonal item has its 128)
+constexpr int kItemQueries = 768;     // list entries per work item (the diagonal item has its 128)
 
 template <typename T, int D>
 struct FwdCfg {
