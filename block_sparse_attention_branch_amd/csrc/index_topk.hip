@@ -285,7 +285,10 @@ __global__ __launch_bounds__(kIdxThreads, (CAP > 31 ? 1 : 2)) void index_topk_ke
     }
   } else {
     // fp32: the accumulators would not fit beside the list registers through
-    // the barrier, which therefore closes the block.
+    // the barrier, which therefore closes the block.  The body is written out
+    // rather than built from the lambdas above: with them the compiler
+    // allocates the fp32 instances differently and several spill far more
+    // (up to 174 VGPRs at topk 64).
     for (int j = 0; j <= jlast; ++j) {
       const int buf = j & 1;
       const bool more = j < jlast;
