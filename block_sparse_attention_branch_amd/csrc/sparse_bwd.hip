@@ -471,8 +471,11 @@ struct Bwd16Cfg {
   static constexpr size_t OFF_QL = OFF_KIT + (size_t)DIDX * PKT * 2;     // item queries: (t << 6) | slot
   static constexpr int KPQ = kW16 / (D / 16);                             // key parts of the dQ product
   static constexpr int PDQ = D + 4;                                       // dQ tile row pitch (fp32)
-  static constexpr size_t OFF_DQ = OFF_QL + (size_t)(kBlock + kBigItem) * 4;   // dQ [KPQ][32][PDQ] fp32
-  static constexpr size_t LDS = OFF_DQ + (size_t)KPQ * 32 * PDQ * 4;
+  // dQ [KPQ][32][PDQ] fp32, only when the dQ product is split over key parts
+  // (d = 64); at d = 128 each wave's product covers all keys and is stored
+  // from registers.
+  static constexpr size_t OFF_DQ = OFF_QL + (size_t)(kBlock + kBigItem) * 4;
+  static constexpr size_t LDS = OFF_DQ + (KPQ > 1 ? (size_t)KPQ * 32 * PDQ * 4 : 0);
   // The flush at the end of an item reuses [0, OFF_QL) as 8 x [16][D + 4] fp32.
   static_assert(OFF_QL >= (size_t)kW16 * 16 * (D + 4) * 4, "flush scratch");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
@@ -750,7 +753,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     if (st > 0) dq_idx_step(st - 1);
     load_step(st + 1);
     peek(st + 2);
-    if (st > 0) dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
+    if constexpr (C::KPQ > 1)
+      if (st > 0) dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
 
     // The two product stretches of the step run at raised wave priority: of
     // two waves of a SIMD in the same stretch, one then runs ahead and reaches
@@ -852,10 +856,13 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     }
     __syncthreads();   // dS^T, dz^T and the KL partials complete
 
-    // dQ[rows, column tile qct] = dS K over key part qkp (lane = column, slots
-    // = rows) into the step's dQ tile in LDS; the tile leaves as bf16 partials
-    // at the top of the next step, whose barrier completes it.  Nothing reads
-    // the tile between the barrier above and this write.
+    // dQ[rows, column tile qct] = dS K over key part qkp.  With one key part
+    // (d = 128) it is computed transposed, dQ^T = K^T dS^T, so that a lane
+    // holds 4 consecutive columns of one row and stores them as the row's
+    // bf16 partial at once.  With two (d = 64) the parts meet in the step's
+    // dQ tile in LDS (lane = column, slots = rows), which leaves as bf16
+    // partials at the top of the next step, whose barrier completes it;
+    // nothing reads the tile between the barrier above and this write.
     {
       // The K operands are read once for both row tiles, and the tile is
       // written after all products (an LDS write between them would make the
@@ -865,19 +872,44 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
       for (int ks = 0; ks < 4 / KPQ; ++ks)   // keys k0 .. k0+3, k0+16 .. k0+19 of the dS^T reads below
         kq[ks] = *reinterpret_cast<const bf16x8*>(Kt + (16 * qct + c) * C::PKT + 32 * (qkp * (4 / KPQ) + ks) + 8 * lq);
       f32x4 o[2];
+      if constexpr (C::KPQ == 1) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        o[t] = zero4();
+        for (int t = 0; t < 2; ++t) {
+          o[t] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 4 / KPQ; ++ks) {
-          const int k0 = 32 * (qkp * (4 / KPQ) + ks) + 4 * lq;
-          o[t] = mma16(tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane), kq[ks], o[t]);
+          for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = 32 * ks + 4 * lq;
+            o[t] = mma16(kq[ks], tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane), o[t]);
+          }
         }
+        // Row 16 t + c, columns 16 qct + 4 lq .. +3.  A row without a query
+        // goes to the spare row n_prow, so the stores are unconditional; every
+        // row index is checked against the partial rows before it becomes an
+        // address.  Ordinary (not streaming) stores: the 8 waves' 32-byte
+        // pieces of a row meet in L2 as whole lines (streaming stores of these
+        // pieces made the kernel 10% slower at N = 128K).
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int id = tb[kRowId * 32 + 16 * t + c];
+          const int dst = (unsigned)id < (unsigned)n_prow ? id : n_prow;
+          *reinterpret_cast<bf16x4*>(dq_part + (size_t)dst * D + 16 * qct + 4 * lq) =
+              pack4(o[t][0], o[t][1], o[t][2], o[t][3]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          o[t] = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 4 / KPQ; ++ks) {
+            const int k0 = 32 * (qkp * (4 / KPQ) + ks) + 4 * lq;
+            o[t] = mma16(tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane), kq[ks], o[t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dQt[(qkp * 32 + 16 * t + 4 * lq + e) * C::PDQ + 16 * qct + c] = o[t][e];
       }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dQt[(qkp * 32 + 16 * t + 4 * lq + e) * C::PDQ + 16 * qct + c] = o[t][e];
     }
     if (EXTRA && kl != nullptr && threadIdx.x < 32) {
       const int id = tb[kQryId * 32 + threadIdx.x];
@@ -892,8 +924,10 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   if constexpr (!EXTRA)
     asm volatile("" : "+v"(lane), "+v"(c), "+v"(lq), "+v"(wave), "+v"(qct), "+v"(qkp), "+v"(ict), "+v"(ikp));
   dq_idx_step(n_steps - 1);   // its dz^T was completed by the loop's last barrier
-  __syncthreads();            // the last step's dQ tile complete
-  dq_store(n_steps - 1);
+  if constexpr (C::KPQ > 1) {
+    __syncthreads();          // the last step's dQ tile complete
+    dq_store(n_steps - 1);
+  }
 
   // Flush the wave's dK, dV (group g) and dk_idx (shared by the groups):
   // C layout [d rows][16 keys] -> LDS [16 keys][d] -> atomics of whole key rows.
