@@ -281,14 +281,15 @@ __global__ __launch_bounds__(256) void idx_lse_merge_kernel(const float2* __rest
 // launch so that the items still outnumber the CUs many times over.
 constexpr int kBigItem = 4096;
 
-// Per-step tables (32 entries each) in LDS, double buffered.
+// Per-step tables (32 entries each) in LDS, double buffered: the row tables
+// by step, the query tables (index rows) by index group.
 enum : int {
   kRowT = 0,     // t of the row, -1 past the item's end
   kRowCut,       // key u is visible to the row iff u <= cut (-1: none)
   kRowLse,       // LSE * log2(e)
   kRowD,         // rowsum(dO * O)
   kRowId,        // dQ partial row ((b CQ + t - c0) topk + slot) H_q + h, or -1
-  kQryT,         // per query of the step: t or -1
+  kQryT,         // per index row (query) of the step or index group: t or -1
   kQrySlot,      // position of block j in the query's selection
   kQryCut,       // visibility cut-off of the query (-1: none)
   kQryLse,       // index LSE * log2(e)
@@ -377,7 +378,8 @@ __device__ inline bf16x4 pack4(float a, float b, float c, float d) {
 // of a step holds R = 8q + 4 tile + v, i.e. query R / G and head R % G, so
 // that the lanes of group q hold whole queries (for G <= 8) and the teacher
 // mean over a query's heads is a sum inside the lane.  The index logits use
-// "query rows" m' = 16 t + 4q + v whose query is ri_query<G>(t, q, v).
+// "query rows" m' = 16 t + 4q + v whose query is ri_query<G>(t, q, v), or,
+// for G >= 8, the query rows of an index group of G / 2 steps (idx_group).
 // ---------------------------------------------------------------------------
 constexpr int kW16 = 8;                        // waves of the 16x16 kernel
 constexpr int kT16 = kW16 * kWave;             // its threads
@@ -420,6 +422,40 @@ __device__ inline int ri_query(int t, int q, int v) {
   if constexpr (G == 1) return 8 * q + 4 * t + v;
   else if constexpr (G <= 8) return (t == 0 && v < 8 / G) ? q * (8 / G) + v : -1;
   else return (t == 0 && v == 0 && (q & 1) == 0) ? q / 2 : -1;
+}
+// Index-logit groups.  With G >= 8 a step holds TQ = 32 / G <= 4 queries and
+// fills at most a quarter of a 16-row index-logit tile.  The index work
+// (logits, dz, dk_idx and dq_idx) then runs once per F = 16 / TQ = G / 2
+// consecutive steps, on one tile whose row 4q + v holds query idx_local of
+// group step idx_step.  That query's teacher mean is in lane group q of the
+// step (slot 0 of head_mean16), so each lane keeps the four means of its
+// rows until the group's last step.  With G <= 4 (F = 1) the tile rows are
+// the ri_query rows of every step: at G = 4, groups of two steps measured
+// slower than the half-empty tiles (B = 4, N = 8K: 5.04 -> 5.2 ms).
+template <int G>
+constexpr int idx_group() { return G >= 8 ? G / 2 : 1; }
+template <int G>
+__device__ inline int idx_step(int q, int v) { return G == 8 ? v : 4 * (q & 1) + v; }
+template <int G>
+__device__ inline int idx_local(int q, int v) { return G == 8 ? q : q >> 1; }
+// What step st of a group (s = st mod F) stores in index row r (0..31): the
+// local query >= 0 to load, -1 to clear the row (no query), -2 to keep it.
+// A group's first step clears every row that a later step of the group
+// fills, so that rows a short item never reaches hold no query.
+template <int G>
+__device__ inline int idx_row_query(int r, int s) {
+  if constexpr (idx_group<G>() == 1) {
+    return ri_query<G>(r >> 4, (r >> 2) & 3, r & 3);
+  } else {
+    if (r < 16 && idx_step<G>(r >> 2, r & 3) == s) return idx_local<G>(r >> 2, r & 3);
+    return s == 0 ? -1 : -2;
+  }
+}
+// Whether index row 16 t + 4 q + v can hold a query.
+template <int G>
+__device__ inline bool idx_row_used(int t, int q, int v) {
+  if constexpr (idx_group<G>() == 1) return ri_query<G>(t, q, v) >= 0;
+  else return t == 0;
 }
 // Teacher: mean of P over each query's heads, at the query rows' C layout.
 template <int G>
@@ -508,6 +544,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   constexpr int DTI = DIDX / 16;    // 16-wide d_idx tiles
   constexpr int TQ = 32 / G;        // queries per 32-row step
   constexpr int NTQ = G == 1 ? 2 : 1;                       // query-row tiles
+  constexpr int F = idx_group<G>();                         // steps per index group
   constexpr int CPR = D / 8;        // 16-byte chunks per Q / dO row
   constexpr int CPRI = DIDX / 8;    // 16-byte chunks per q_idx row
   constexpr int NT = kNumTabs * 32;
@@ -593,9 +630,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   const int ld_rr = row_r(ld_m >> 4, (ld_m >> 2) & 3, ld_m & 3);   // R of the thread's row
   const bool ld_qi = tx < 32 * CPRI;
   const int ld_mi = (tx / CPRI) & 31, ld_qcol = (tx % CPRI) * 8;
-  const int ld_qq = ri_query<G>(ld_mi >> 4, (ld_mi >> 2) & 3, ld_mi & 3);
   const int mq = tx & 31;
-  const int mq_q = ri_query<G>(mq >> 4, (mq >> 2) & 3, mq & 3);
   struct Pre {
     bf16x8 q, d, qi;
     float lse, rd, qlse;
@@ -607,8 +642,9 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   auto cutoff = [&](int qi, int t) { return t < 0 ? -1 : ((qi < it.n_own && causal) ? t : 0x7fffffff); };
   auto peek = [&](int st) {
     pk_e = ld_row ? entry(st * TQ + ld_rr / G) : -1;
-    pk_qi = (ld_qi && ld_qq >= 0) ? entry(st * TQ + ld_qq) : -1;
-    pk_qt = (tx < 32 && mq_q >= 0) ? entry(st * TQ + mq_q) : -1;
+    const int lqi = idx_row_query<G>(ld_mi, st & (F - 1)), lqt = idx_row_query<G>(mq, st & (F - 1));
+    pk_qi = (ld_qi && lqi >= 0) ? entry(st * TQ + lqi) : -1;
+    pk_qt = (tx < 32 && lqt >= 0) ? entry(st * TQ + lqt) : -1;
   };
   // Unconditional loads (clamped to a valid row): the compiler counts them.
   // Row indices are 32-bit (B N H_q < 2^31, checked by the host), with the
@@ -644,7 +680,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     {
       pre.qt = pk_qt < 0 ? -1 : (pk_qt >> 6);
       pre.qslot = pk_qt < 0 ? 0 : (pk_qt & 63);
-      pre.qcut = cutoff(st * TQ + (mq_q < 0 ? 0 : mq_q), pre.qt);
+      pre.qcut = cutoff(st * TQ + max(idx_row_query<G>(mq, st & (F - 1)), 0), pre.qt);
       const int qrow = (bN + max(pre.qt, 0)) * H_kv + g;
       pre.qid = pre.qt < 0 ? -1 : qrow;
       pre.qlse = lse_idx[qrow];
@@ -664,14 +700,17 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         tb[kRowId * 32 + ld_m] = pre.id;
       }
     }
-    if (ld_qi) *reinterpret_cast<bf16x8*>(QIs + C::TI::off(ld_mi, ld_qcol)) = pre.qi;
-    if (tx < 32) {
-      tb[kQryT * 32 + tx] = pre.qt;
-      tb[kQrySlot * 32 + tx] = pre.qslot;
-      tb[kQryCut * 32 + tx] = pre.qcut;
-      tf[kQryLse * 32 + tx] = pre.qlse * kLog2e;
-      tf[kQryKl * 32 + tx] = 0.f;
-      tb[kQryId * 32 + tx] = pre.qid;
+    if (ld_qi && idx_row_query<G>(ld_mi, st & (F - 1)) != -2)
+      *reinterpret_cast<bf16x8*>(QIs + C::TI::off(ld_mi, ld_qcol)) = pre.qi;
+    int* tg = tabs + ((st / F) & 1) * NT;   // the query tables of the step's index group
+    float* tgf = reinterpret_cast<float*>(tg);
+    if (tx < 32 && idx_row_query<G>(mq, st & (F - 1)) != -2) {
+      tg[kQryT * 32 + tx] = pre.qt;
+      tg[kQrySlot * 32 + tx] = pre.qslot;
+      tg[kQryCut * 32 + tx] = pre.qcut;
+      tgf[kQryLse * 32 + tx] = pre.qlse * kLog2e;
+      tgf[kQryKl * 32 + tx] = 0.f;
+      tg[kQryId * 32 + tx] = pre.qid;
     }
   };
 
@@ -679,18 +718,18 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   const float c_i = scale_idx * kLog2e;
   const int n_steps = (nq * G + 31) / 32;
   // dq_idx[query rows, column tile ict] = dz K_idx over the block's keys, for
-  // step st.  It runs at the top of step st + 1, before that step's loads are
-  // issued: its atomics are conditional, so the compiler cannot count them, and
-  // there they sit behind no load that has to be waited for (dz^T is double
-  // buffered for it).
+  // the index group that ends at step st.  It runs at the top of step st + 1,
+  // before that step's loads are issued: its atomics are conditional, so the
+  // compiler cannot count them, and there they sit behind no load that has to
+  // be waited for (dz^T is double buffered for it, by group).
   auto dq_idx_step = [&](int st) {
     // The waves of key part 0 take all 128 keys of their column tile and the
     // others skip, so each dq_idx value gets one atomic per step rather than
     // one per key part (at d_idx = 64 a skipping wave shares its SIMD with a
     // working one).
     if (ikp != 0) return;
-    const int* tb = tabs + (st & 1) * NT;
-    const bf16* dZt = dZt2 + (st & 1) * kBlock * C::PST;
+    const int* tb = tabs + ((st / F) & 1) * NT;
+    const bf16* dZt = dZt2 + ((st / F) & 1) * kBlock * C::PST;
     f32x4 o[NTQ];
 #pragma unroll
     for (int t = 0; t < NTQ; ++t) {
@@ -706,7 +745,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     for (int t = 0; t < NTQ; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (ri_query<G>(t, lq, e) >= 0) {
+        if (idx_row_used<G>(t, lq, e)) {
           const int id = tb[kQryId * 32 + 16 * t + 4 * lq + e];
           if ((unsigned)id < (unsigned)n_grows) atomicAdd(dq_idx + (size_t)id * DIDX + 16 * ict + c, o[t][e]);
         }
@@ -740,6 +779,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
       __builtin_nontemporal_store(y, reinterpret_cast<bf16x8*>(dq_part + (size_t)dst * D + col));
     }
   };
+  f32x4 pbh = zero4();   // teacher means of the lane's index rows (F > 1)
   peek(0);
   load_step(0);
   store_step(0);
@@ -750,7 +790,12 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     const int* tb = tabs + (st & 1) * NT;
     const float* tf = reinterpret_cast<const float*>(tb);
     __syncthreads();   // step st's tiles and tables in LDS; step st-1's dS^T / dz^T complete
-    if (st > 0) dq_idx_step(st - 1);
+    if (st > 0 && ((st - 1) & (F - 1)) == F - 1) dq_idx_step(st - 1);   // a group ended at step st - 1
+    // Index work in this step: every step with F = 1, else a group's last
+    // step and the item's last step (which may end a group early).
+    const bool idx_now = F == 1 || (st & (F - 1)) == F - 1 || st == n_steps - 1;
+    const int* tg = tabs + ((st / F) & 1) * NT;   // the index group's query tables
+    const float* tgf = reinterpret_cast<const float*>(tg);
     load_step(st + 1);
     peek(st + 2);
     if constexpr (C::KPQ > 1)
@@ -777,6 +822,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 #pragma unroll
     for (int t = 0; t < NTQ; ++t) {
       ri[t] = zero4();
+      if (!idx_now) continue;
 #pragma unroll
       for (int ks = 0; ks < KSI; ++ks) {
         const int col = 32 * ks + 8 * lq;
@@ -809,11 +855,19 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     // Teacher, p_px, dz on the query rows; dz^T to LDS.
     f32x4 pb[NTQ], dz[NTQ];
     head_mean16<G>(p, pb);
+    if constexpr (F > 1) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (idx_step<G>(lq, v) == (st & (F - 1))) pbh[v] = pb[0][0];
+      pb[0] = pbh;
+    }
 #pragma unroll
     for (int t = 0; t < NTQ; ++t) {
+      dz[t] = zero4();
+      if (!idx_now) continue;
       const int r4 = 16 * t + 4 * lq;
-      const int4 qc = *reinterpret_cast<const int4*>(tb + kQryCut * 32 + r4);
-      const f32x4 ql = *(const volatile lds_f32x4*)(tf + kQryLse * 32 + r4);
+      const int4 qc = *reinterpret_cast<const int4*>(tg + kQryCut * 32 + r4);
+      const f32x4 ql = *(const volatile lds_f32x4*)(tgf + kQryLse * 32 + r4);
       const int qcs[4] = {qc.x, qc.y, qc.z, qc.w};
       const float qls[4] = {ql[0], ql[1], ql[2], ql[3]};
 #pragma unroll
@@ -823,7 +877,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         const float ez = __builtin_amdgcn_exp2f(vis ? lz : -INFINITY);
         dz[t][e] = vis ? lam * (ez - pb[t][e]) : 0.f;
         if (EXTRA && dscore != nullptr && vis) {
-          const int tq = tb[kQryT * 32 + r4 + e], sl = tb[kQrySlot * 32 + r4 + e];
+          const int tq = tg[kQryT * 32 + r4 + e], sl = tg[kQrySlot * 32 + r4 + e];
           if ((unsigned)tq < (unsigned)N && (unsigned)sl < (unsigned)topk)
             dscore[((((size_t)b * N + tq) * H_kv + g) * topk + sl) * kBlock + key] = dz[t][e];
         }
@@ -832,10 +886,10 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
 #pragma unroll
           for (int off = 8; off > 0; off >>= 1) klv += __shfl_xor(klv, off);   // over the lane group's 16 keys
           if (c == 0 && qcs[e] >= 0)
-            atomicAdd(reinterpret_cast<float*>(tabs + (st & 1) * NT) + kQryKl * 32 + r4 + e, klv);
+            atomicAdd(reinterpret_cast<float*>(tabs + ((st / F) & 1) * NT) + kQryKl * 32 + r4 + e, klv);
         }
       }
-      *reinterpret_cast<bf16x4*>(dZt2 + (st & 1) * kBlock * C::PST + key * C::PST + r4) =
+      *reinterpret_cast<bf16x4*>(dZt2 + ((st / F) & 1) * kBlock * C::PST + key * C::PST + r4) =
           pack4(dz[t][0] * scale_idx, dz[t][1] * scale_idx, dz[t][2] * scale_idx, dz[t][3] * scale_idx);
     }
     // dV^T += dO^T P, dK^T += Q^T dS (K = the 32 rows, in the order of the
@@ -849,9 +903,10 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         acc_dk[dt] = mma16(tr16<typename C::TQ>(Qs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), sbf, acc_dk[dt]);
       }
       const bf16x8 zb = cpair(dz[0] * scale_idx, NTQ == 2 ? dz[NTQ - 1] * scale_idx : zero4());
+      if (idx_now)
 #pragma unroll
-      for (int dt = 0; dt < DTI; ++dt)
-        acc_dki[dt] = mma16(tr16<typename C::TI>(QIs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), zb, acc_dki[dt]);
+        for (int dt = 0; dt < DTI; ++dt)
+          acc_dki[dt] = mma16(tr16<typename C::TI>(QIs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), zb, acc_dki[dt]);
       __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();   // dS^T, dz^T and the KL partials complete
@@ -911,9 +966,9 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
           for (int e = 0; e < 4; ++e) dQt[(qkp * 32 + 16 * t + 4 * lq + e) * C::PDQ + 16 * qct + c] = o[t][e];
       }
     }
-    if (EXTRA && kl != nullptr && threadIdx.x < 32) {
-      const int id = tb[kQryId * 32 + threadIdx.x];
-      if ((unsigned)id < (unsigned)n_grows) atomicAdd(&kl[id], tf[kQryKl * 32 + threadIdx.x]);
+    if (EXTRA && kl != nullptr && idx_now && threadIdx.x < 32) {
+      const int id = tg[kQryId * 32 + threadIdx.x];
+      if ((unsigned)id < (unsigned)n_grows) atomicAdd(&kl[id], tgf[kQryKl * 32 + threadIdx.x]);
     }
     store_step(st + 1);
   }
