@@ -510,7 +510,10 @@ struct Bwd16Cfg {
   // dQ [KPQ][32][PDQ] fp32, only when the dQ product is split over key parts
   // (d = 64); at d = 128 each wave's product covers all keys and is stored
   // from registers.
-  static constexpr size_t OFF_DQ = OFF_QL + (size_t)(kBlock + kBigItem) * 4;
+  // The list is followed by kQlPad entries of -1, so that the step loop's
+  // look-ahead past the item's end reads them instead of testing its index.
+  static constexpr int kQlPad = 128;
+  static constexpr size_t OFF_DQ = OFF_QL + (size_t)(kBlock + kBigItem + kQlPad) * 4;
   static constexpr size_t LDS = OFF_DQ + (KPQ > 1 ? (size_t)KPQ * 32 * PDQ * 4 : 0);
   // The flush at the end of an item reuses [0, OFF_QL) as 8 x [16][D + 4] fp32.
   static_assert(OFF_QL >= (size_t)kW16 * 16 * (D + 4) * 4, "flush scratch");
@@ -578,10 +581,10 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   const size_t blk_row0 = ((size_t)b * N + (size_t)j * kBlock) * H_kv + g;   // key 0 of the block
   const int nq = it.n_own + it.ne;   // >= 1: an item holds its diagonal queries or list entries
 
-  for (int qi = threadIdx.x; qi < nq; qi += kT16) {
+  for (int qi = threadIdx.x; qi < nq + C::kQlPad; qi += kT16) {
     int slot;
     const int t = big_query(it, qi, block_idx, N, H_kv, topk, &slot);
-    qlist[qi] = t < 0 ? -1 : ((t << 6) | slot);
+    qlist[qi] = (qi >= nq || t < 0) ? -1 : ((t << 6) | slot);
   }
   // K and K_idx transposed (keys in kt_pos order) for the B operands of the
   // dQ and dq_idx products; K_idx also row-major for the index logits.
@@ -638,7 +641,9 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   };
   Pre pre;
   int pk_e = -1, pk_qi = -1, pk_qt = -1;
-  auto entry = [&](int qi) { return qi < nq ? qlist[qi] : -1; };
+  // Look-ahead indices stay below nq + 3 * TQ <= nq + 96 (two steps ahead
+  // of the last, each of at most 32 queries), inside the padding.
+  auto entry = [&](int qi) { return qlist[qi]; };
   auto cutoff = [&](int qi, int t) { return t < 0 ? -1 : ((qi < it.n_own && causal) ? t : 0x7fffffff); };
   auto peek = [&](int st) {
     pk_e = ld_row ? entry(st * TQ + ld_rr / G) : -1;
@@ -695,7 +700,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
       if (ld_col == 0) {
         tb[kRowT * 32 + ld_m] = pre.t;
         tb[kRowCut * 32 + ld_m] = pre.cut;
-        tf[kRowLse * 32 + ld_m] = pre.lse * kLog2e;
+        tf[kRowLse * 32 + ld_m] = pre.t < 0 ? INFINITY : pre.lse * kLog2e;   // no query: P = 0
         tf[kRowD * 32 + ld_m] = pre.rd;
         tb[kRowId * 32 + ld_m] = pre.id;
       }
@@ -801,13 +806,65 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
     if constexpr (C::KPQ > 1)
       if (st > 0) dq_store(st - 1);   // after the loads: the wait for them at the step's end skips it
 
+    // Index work on the query rows (NTQ tiles; lane = key, slots = rows):
+    // the logits, p_px and dz (with dz^T to LDS), and dk_idx^T += q_idx^T dz.
+    auto idx_logits = [&](f32x4* ri) {
+#pragma unroll
+      for (int t = 0; t < NTQ; ++t) {
+        ri[t] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KSI; ++ks) {
+          const int col = 32 * ks + 8 * lq;
+          ri[t] = mma16(*reinterpret_cast<const bf16x8*>(QIs + C::TI::off(16 * t + c, col)),
+                        *reinterpret_cast<const bf16x8*>(KIs + C::TI::off(key, col)), ri[t]);
+        }
+      }
+    };
+    auto idx_dz = [&](const f32x4* ri, const f32x4* pb, f32x4* dz) {
+#pragma unroll
+      for (int t = 0; t < NTQ; ++t) {
+        const int r4 = 16 * t + 4 * lq;
+        const int4 qc = *reinterpret_cast<const int4*>(tg + kQryCut * 32 + r4);
+        const f32x4 ql = *(const volatile lds_f32x4*)(tgf + kQryLse * 32 + r4);
+        const int qcs[4] = {qc.x, qc.y, qc.z, qc.w};
+        const float qls[4] = {ql[0], ql[1], ql[2], ql[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lz = ri[t][e] * c_i - qls[e];     // log2 p_px
+          const bool vis = u <= qcs[e];                  // -1 for rows that hold no query
+          const float ez = __builtin_amdgcn_exp2f(vis ? lz : -INFINITY);
+          dz[t][e] = vis ? lam * (ez - pb[t][e]) : 0.f;
+          if (EXTRA && dscore != nullptr && vis) {
+            const int tq = tg[kQryT * 32 + r4 + e], sl = tg[kQrySlot * 32 + r4 + e];
+            if ((unsigned)tq < (unsigned)N && (unsigned)sl < (unsigned)topk)
+              dscore[((((size_t)b * N + tq) * H_kv + g) * topk + sl) * kBlock + key] = dz[t][e];
+          }
+          if (EXTRA && kl != nullptr) {
+            float klv = (vis && pb[t][e] > 0.f) ? pb[t][e] * (logf(pb[t][e]) - lz * kLn2) : 0.f;
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) klv += __shfl_xor(klv, off);   // over the lane group's 16 keys
+            if (c == 0 && qcs[e] >= 0)
+              atomicAdd(reinterpret_cast<float*>(tabs + ((st / F) & 1) * NT) + kQryKl * 32 + r4 + e, klv);
+          }
+        }
+        *reinterpret_cast<bf16x4*>(dZt2 + ((st / F) & 1) * kBlock * C::PST + key * C::PST + r4) =
+            pack4(dz[t][0] * scale_idx, dz[t][1] * scale_idx, dz[t][2] * scale_idx, dz[t][3] * scale_idx);
+      }
+    };
+    auto idx_dki = [&](const f32x4* dz) {
+      const bf16x8 zb = cpair(dz[0] * scale_idx, NTQ == 2 ? dz[NTQ - 1] * scale_idx : zero4());
+#pragma unroll
+      for (int dt = 0; dt < DTI; ++dt)
+        acc_dki[dt] = mma16(tr16<typename C::TI>(QIs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), zb, acc_dki[dt]);
+    };
+
     // The two product stretches of the step run at raised wave priority: of
     // two waves of a SIMD in the same stretch, one then runs ahead and reaches
     // its vector work while the other still issues products.
-    // S, dP (two row tiles) and the index logits (NTQ query-row tiles): lane
-    // = key, slots = rows.
+    // S, dP (two row tiles; lane = key, slots = rows), with the index logits
+    // when every step runs the index work (F = 1).
     __builtin_amdgcn_s_setprio(1);
-    f32x4 s[2], dp[2], ri[NTQ];
+    f32x4 s[2], dp[2], ri[NTQ], dz[NTQ];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = zero4();
@@ -819,78 +876,54 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         dp[t] = mma16(*reinterpret_cast<const bf16x8*>(dOs + C::TQ::off(16 * t + c, col)), vfr[ks], dp[t]);
       }
     }
-#pragma unroll
-    for (int t = 0; t < NTQ; ++t) {
-      ri[t] = zero4();
-      if (!idx_now) continue;
-#pragma unroll
-      for (int ks = 0; ks < KSI; ++ks) {
-        const int col = 32 * ks + 8 * lq;
-        ri[t] = mma16(*reinterpret_cast<const bf16x8*>(QIs + C::TI::off(16 * t + c, col)),
-                      *reinterpret_cast<const bf16x8*>(KIs + C::TI::off(key, col)), ri[t]);
-      }
-    }
+    if constexpr (F == 1) idx_logits(ri);
     __builtin_amdgcn_s_setprio(0);
-    // P, dS; dS^T to LDS (rows 16 t + 4 lq .. +3 of this lane's key).
+    // P, dS; dS^T to LDS (rows 16 t + 4 lq .. +3 of this lane's key).  Only
+    // the steps holding the block's own queries (causal) test each key
+    // against the row's cut-off; a row without a query has LSE = +inf, so
+    // its P is exp2(-inf) = 0 either way.
     f32x4 p[2], ds[2];
+    auto p_ds = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r4 = 16 * t + 4 * lq;
-      const int4 cut = *reinterpret_cast<const int4*>(tb + kRowCut * 32 + r4);
-      // Volatile: read whole and up front, never sunk into the masked use.
-      const f32x4 l2 = *(const volatile lds_f32x4*)(tf + kRowLse * 32 + r4);
-      const float4 dd = *reinterpret_cast<const float4*>(tf + kRowD * 32 + r4);
-      const int cuts[4] = {cut.x, cut.y, cut.z, cut.w};
-      const float l2s[4] = {l2[0], l2[1], l2[2], l2[3]};
-      const float dds[4] = {dd.x, dd.y, dd.z, dd.w};
+      for (int t = 0; t < 2; ++t) {
+        const int r4 = 16 * t + 4 * lq;
+        int cuts[4] = {0, 0, 0, 0};
+        if constexpr (MASKED) {
+          const int4 cut = *reinterpret_cast<const int4*>(tb + kRowCut * 32 + r4);
+          cuts[0] = cut.x; cuts[1] = cut.y; cuts[2] = cut.z; cuts[3] = cut.w;
+        }
+        // Volatile: read whole and up front, never sunk into the masked use.
+        const f32x4 l2 = *(const volatile lds_f32x4*)(tf + kRowLse * 32 + r4);
+        const float4 dd = *reinterpret_cast<const float4*>(tf + kRowD * 32 + r4);
+        const float l2s[4] = {l2[0], l2[1], l2[2], l2[3]};
+        const float dds[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // Masked by the exponent (exp2(-inf) = 0), so no branch is formed.
-        const float pv = __builtin_amdgcn_exp2f(u <= cuts[e] ? s[t][e] * c_s - l2s[e] : -INFINITY);
-        p[t][e] = pv;
-        ds[t][e] = pv * (dp[t][e] - dds[e]) * scale;
+        for (int e = 0; e < 4; ++e) {
+          // Masked by the exponent (exp2(-inf) = 0), so no branch is formed.
+          const float x = s[t][e] * c_s - l2s[e];
+          const float pv = __builtin_amdgcn_exp2f(MASKED ? (u <= cuts[e] ? x : -INFINITY) : x);
+          p[t][e] = pv;
+          ds[t][e] = pv * (dp[t][e] - dds[e]) * scale;
+        }
+        *reinterpret_cast<bf16x4*>(dSt + key * C::PST + r4) = pack4(ds[t][0], ds[t][1], ds[t][2], ds[t][3]);
       }
-      *reinterpret_cast<bf16x4*>(dSt + key * C::PST + r4) = pack4(ds[t][0], ds[t][1], ds[t][2], ds[t][3]);
-    }
-    // Teacher, p_px, dz on the query rows; dz^T to LDS.
-    f32x4 pb[NTQ], dz[NTQ];
+    };
+    // (At G = 16, and in the instances with per-score outputs, the two
+    // versions of this code cost spilled registers, so those keep the masked
+    // one for every step.)
+    if (EXTRA || G > 8 || (causal && st * TQ < it.n_own)) p_ds(std::true_type{});
+    else p_ds(std::false_type{});
+    // Teacher p̄ on the query rows; with F > 1 each lane keeps the means of
+    // its index rows until the group's last step.
+    f32x4 pb[NTQ];
     head_mean16<G>(p, pb);
-    if constexpr (F > 1) {
+    if constexpr (F == 1) {
+      idx_dz(ri, pb, dz);
+    } else {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (idx_step<G>(lq, v) == (st & (F - 1))) pbh[v] = pb[0][0];
-      pb[0] = pbh;
-    }
-#pragma unroll
-    for (int t = 0; t < NTQ; ++t) {
-      dz[t] = zero4();
-      if (!idx_now) continue;
-      const int r4 = 16 * t + 4 * lq;
-      const int4 qc = *reinterpret_cast<const int4*>(tg + kQryCut * 32 + r4);
-      const f32x4 ql = *(const volatile lds_f32x4*)(tgf + kQryLse * 32 + r4);
-      const int qcs[4] = {qc.x, qc.y, qc.z, qc.w};
-      const float qls[4] = {ql[0], ql[1], ql[2], ql[3]};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lz = ri[t][e] * c_i - qls[e];     // log2 p_px
-        const bool vis = u <= qcs[e];                  // -1 for rows that hold no query
-        const float ez = __builtin_amdgcn_exp2f(vis ? lz : -INFINITY);
-        dz[t][e] = vis ? lam * (ez - pb[t][e]) : 0.f;
-        if (EXTRA && dscore != nullptr && vis) {
-          const int tq = tg[kQryT * 32 + r4 + e], sl = tg[kQrySlot * 32 + r4 + e];
-          if ((unsigned)tq < (unsigned)N && (unsigned)sl < (unsigned)topk)
-            dscore[((((size_t)b * N + tq) * H_kv + g) * topk + sl) * kBlock + key] = dz[t][e];
-        }
-        if (EXTRA && kl != nullptr) {
-          float klv = (vis && pb[t][e] > 0.f) ? pb[t][e] * (logf(pb[t][e]) - lz * kLn2) : 0.f;
-#pragma unroll
-          for (int off = 8; off > 0; off >>= 1) klv += __shfl_xor(klv, off);   // over the lane group's 16 keys
-          if (c == 0 && qcs[e] >= 0)
-            atomicAdd(reinterpret_cast<float*>(tabs + ((st / F) & 1) * NT) + kQryKl * 32 + r4 + e, klv);
-        }
-      }
-      *reinterpret_cast<bf16x4*>(dZt2 + ((st / F) & 1) * kBlock * C::PST + key * C::PST + r4) =
-          pack4(dz[t][0] * scale_idx, dz[t][1] * scale_idx, dz[t][2] * scale_idx, dz[t][3] * scale_idx);
     }
     // dV^T += dO^T P, dK^T += Q^T dS (K = the 32 rows, in the order of the
     // two tiles' slots), dk_idx^T += q_idx^T dz.
@@ -902,12 +935,17 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         acc_dv[dt] = mma16(tr16<typename C::TQ>(dOs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), pbf, acc_dv[dt]);
         acc_dk[dt] = mma16(tr16<typename C::TQ>(Qs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), sbf, acc_dk[dt]);
       }
-      const bf16x8 zb = cpair(dz[0] * scale_idx, NTQ == 2 ? dz[NTQ - 1] * scale_idx : zero4());
-      if (idx_now)
-#pragma unroll
-        for (int dt = 0; dt < DTI; ++dt)
-          acc_dki[dt] = mma16(tr16<typename C::TI>(QIs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), zb, acc_dki[dt]);
+      if constexpr (F == 1) idx_dki(dz);
       __builtin_amdgcn_s_setprio(0);
+    }
+    // With F > 1 the group's index work, once, on its last step.
+    if constexpr (F > 1) {
+      if (idx_now) {
+        const f32x4 pbg[1] = {pbh};
+        idx_logits(ri);
+        idx_dz(ri, pbg, dz);
+        idx_dki(dz);
+      }
     }
     __syncthreads();   // dS^T, dz^T and the KL partials complete
 
