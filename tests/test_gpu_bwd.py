@@ -7,7 +7,10 @@ slice where a local error would hide: per (query row, group) for dq, dq_idx
 and dscore, per (KV block, group) for dk and dv, per KV block for dk_idx.  A
 slice whose oracle value is zero must be (near) zero on the GPU too.  The KL
 value per row within 2e-2 absolute.  Properties checked at any size: per row
-the index-logit gradient sums to zero (sum p_px = sum pbar = 1).
+the index-logit gradient sums to zero (sum p_px = sum pbar = 1).  The small
+full cases also run the kernel instance without the per-score outputs (the
+one a training step runs, which skips the causal test off the diagonal) and
+hold it to the same per-slice bar.
 
 The backward forms D = rowsum(dO * o) from the o it is given, as the
 FlashAttention backward does.  The per-row dq bar therefore runs with the
@@ -162,6 +165,22 @@ def _full(w, causal=True, lam=1.0):
         # Property: per (b, t, g) the index-logit gradient sums to zero.
         zsum = got["dscore"].sum(axis=(3, 4))
         assert np.abs(zsum).max() <= 1e-3 * max(1.0, abs(lam))
+        if mode == "isolated":
+            # The kernel instance without the per-score outputs (the one a
+            # training step runs) against the same reference.
+            gp = _bwd(w, x, sel, o_in.to(DEV), lse_in.to(DEV), causal, lam=lam)
+            say(" isolated, without dscore / kl:")
+            gotp = {n: f32(gp[n]) for n in ("dq", "dk", "dv", "dq_idx", "dk_idx")}
+            for name in gotp:
+                _cmp(name, gotp[name], ref[name])
+            _slices_cos("dq", _per_row_group(gotp["dq"].reshape(w.B, w.N, H, -1), H),
+                        _per_row_group(ref["dq"].reshape(w.B, w.N, H, -1), H), "(row, group)")
+            _slices_cos("dq_idx", _per_row_group(gotp["dq_idx"], H), _per_row_group(ref["dq_idx"], H),
+                        "(row, group)")
+            for name in ("dk", "dv"):
+                _slices_cos(name, _per_block_group(gotp[name], bs), _per_block_group(ref[name], bs),
+                            "(block, group)")
+            _slices_cos("dk_idx", _per_block(gotp["dk_idx"], bs), _per_block(ref["dk_idx"], bs), "block")
 
 
 @pytest.mark.parametrize("G,d,d_idx", [(1, 128, 64), (2, 64, 32), (4, 128, 64), (8, 128, 64), (16, 64, 64),
