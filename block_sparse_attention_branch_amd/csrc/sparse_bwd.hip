@@ -729,9 +729,9 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
   // be waited for (dz^T is double buffered for it, by group).
   auto dq_idx_step = [&](int st) {
     // The waves of key part 0 take all 128 keys of their column tile and the
-    // others skip, so each dq_idx value gets one atomic per step rather than
-    // one per key part (at d_idx = 64 a skipping wave shares its SIMD with a
-    // working one).
+    // others skip, so each dq_idx value gets one atomic per index group
+    // rather than one per key part (at d_idx = 64 a skipping wave shares its
+    // SIMD with a working one).
     if (ikp != 0) return;
     const int* tb = tabs + ((st / F) & 1) * NT;
     const bf16* dZt = dZt2 + ((st / F) & 1) * kBlock * C::PST;
