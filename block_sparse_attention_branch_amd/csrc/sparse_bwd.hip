@@ -858,8 +858,8 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         acc_dki[dt] = mma16(tr16<typename C::TI>(QIs, 16 * dt, 4 * lq, 16 + 4 * lq, lane), zb, acc_dki[dt]);
     };
 
-    // The two product stretches of the step run at raised wave priority: of
-    // two waves of a SIMD in the same stretch, one then runs ahead and reaches
+    // The product stretches of the step run at raised wave priority: of two
+    // waves of a SIMD in the same stretch, one then runs ahead and reaches
     // its vector work while the other still issues products.
     // S, dP (two row tiles; lane = key, slots = rows), with the index logits
     // when every step runs the index work (F = 1).
@@ -966,6 +966,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
         kq[ks] = *reinterpret_cast<const bf16x8*>(Kt + (16 * qct + c) * C::PKT + 32 * (qkp * (4 / KPQ) + ks) + 8 * lq);
       f32x4 o[2];
       if constexpr (C::KPQ == 1) {
+        __builtin_amdgcn_s_setprio(1);   // as for the other product stretches
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           o[t] = zero4();
@@ -975,6 +976,7 @@ __global__ __launch_bounds__(kT16, 2) void bwd_main16_kernel(
             o[t] = mma16(kq[ks], tr16<typename C::TS>(dSt, 16 * t, k0, k0 + 16, lane), o[t]);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         // Row 16 t + c, columns 16 qct + 4 lq .. +3.  A row without a query
         // goes to the spare row n_prow, so the stores are unconditional; every
         // row index is checked against the partial rows before it becomes an
