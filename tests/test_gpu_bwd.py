@@ -424,6 +424,23 @@ def test_bwd_1m_heavy_lists_across_chunks():
     _heavy(w, 64, 51)
 
 
+def test_bwd_d64_heavy_lists():
+    # d = 64, d_idx = 32: each wave's dQ product covers half the keys and the
+    # halves meet in an LDS tile; blocks 0 .. 14 hold every query of their
+    # (batch, group), 8064 entries, several work items each.
+    w = msa_inputs.Workload("bwd-heavy-d64", B=2, N=8192, H_q=16, H_kv=4, d=64, d_idx=32, topk=16,
+                            backward=True, seed=61)
+    _heavy(w, 64, 61)
+
+
+def test_bwd_g16_heavy_lists():
+    # 16 query heads per group: the index work runs once per 8 steps, over
+    # lists of 16256 entries.
+    w = msa_inputs.Workload("bwd-heavy-g16", B=1, N=16384, H_q=32, H_kv=2, d=128, d_idx=64, topk=16,
+                            backward=True, seed=62)
+    _heavy(w, 64, 62)
+
+
 def test_bwd_dq_and_forward_deterministic():
     """dq is summed from per-block partials in a fixed order, and the forward
     merges its partials in slot order: both are bit-identical across calls
