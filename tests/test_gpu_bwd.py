@@ -245,11 +245,11 @@ def _check_rows(w, gr, ref, bt):
     _slices_cos("dq_idx", _per_row_group(dqi, H), _per_row_group(ref["dq_idx"], H), "(row, group)")
 
 
-def _sampled(w, variant, n_rows, seed, blocks):
+def _sampled(w, variant, n_rows, seed, blocks, causal=True):
     """Rows: dq, dq_idx, kl of sampled rows.  Blocks: dk, dv and dk_idx of
     sampled KV blocks of batch 0, recomputed from every row that selected
     them."""
-    x, sel, o, lse = _fwd(w, variant)
+    x, sel, o, lse = _fwd(w, variant, causal=causal)
     seams = _seams(w)
     rows = sample_rows(w.B, w.N, n_rows, seed, extra=seams)
     say(f"  {len(seams)} seam rows")
@@ -257,13 +257,13 @@ def _sampled(w, variant, n_rows, seed, blocks):
     s = sel.cpu().numpy().astype(np.int64)
     # The sampled rows' o and lse come from the oracle, so that both sides
     # form those rows' D from the same o.
-    o_in, lse_in = _oracle_output(w, x, s, rows=rows)
+    o_in, lse_in = _oracle_output(w, x, s, rows=rows, causal=causal)
     o[bt[:, 0], bt[:, 1]] = o_in.to(DEV)
     lse[bt[:, 0], bt[:, 1]] = lse_in.to(DEV)
-    gr = _bwd(w, x, sel, o, lse, want_kl=True)
+    gr = _bwd(w, x, sel, o, lse, causal, want_kl=True)
     k_h, v_h, ki_h = f32(x["k"]), f32(x["v"]), f32(x["k_idx"])
     ref = O.sparse_bwd(f32(x["q"][bt[:, 0], bt[:, 1]]), k_h, v_h, f32(x["dO"][bt[:, 0], bt[:, 1]]),
-                       f32(x["q_idx"][bt[:, 0], bt[:, 1]]), ki_h, s, w.block_size, True, rows=rows,
+                       f32(x["q_idx"][bt[:, 0], bt[:, 1]]), ki_h, s, w.block_size, causal, rows=rows,
                        o=f32(o_in))
     _check_rows(w, gr, ref, bt)
     dkl = float(np.abs(f32(gr["kl"][bt[:, 0], bt[:, 1]]) - ref["kl"]).max())
@@ -276,7 +276,7 @@ def _sampled(w, variant, n_rows, seed, blocks):
         bti = torch.tensor(brow, dtype=torch.long)
         say(f"  block {j}: {len(brow)} selecting rows")
         rb = O.sparse_bwd(f32(x["q"][bti[:, 0], bti[:, 1]]), k_h, v_h, f32(x["dO"][bti[:, 0], bti[:, 1]]),
-                          f32(x["q_idx"][bti[:, 0], bti[:, 1]]), ki_h, s, bs, True, rows=brow)
+                          f32(x["q_idx"][bti[:, 0], bti[:, 1]]), ki_h, s, bs, causal, rows=brow)
         ks = slice(j * bs, (j + 1) * bs)
         for name in ("dk", "dv"):
             g_, r_ = f32(gr[name][0, ks]), rb[name][0, ks]
@@ -343,19 +343,19 @@ def _heavy_inputs(w, rows, seed):
     return x
 
 
-def _heavy(w, n_rows, seed):
+def _heavy(w, n_rows, seed, causal=True):
     rows = sample_rows(w.B, w.N, n_rows, seed, extra=_seams(w))
     x = _heavy_inputs(w, rows, seed)
-    x, sel, o, lse = _fwd(w, "normal", x=x)
+    x, sel, o, lse = _fwd(w, "normal", causal=causal, x=x)
     bs, H = w.block_size, w.H_kv
     s = sel.cpu().numpy().astype(np.int64)
     # Only the sampled rows have dO != 0 (D = 0 elsewhere); their o and lse
     # come from the oracle, so that both sides form D from the same o.
     bt = torch.tensor(rows, dtype=torch.long)
-    o_in, lse_in = _oracle_output(w, x, s, rows=rows)
+    o_in, lse_in = _oracle_output(w, x, s, rows=rows, causal=causal)
     o[bt[:, 0], bt[:, 1]] = o_in.to(DEV)
     lse[bt[:, 0], bt[:, 1]] = lse_in.to(DEV)
-    gr = _bwd(w, x, sel, o, lse)
+    gr = _bwd(w, x, sel, o, lse, causal)
     # The construction: every row past block 0 selected block 0, so block 0's
     # list holds N - bs entries per (batch, group).
     t = torch.arange(w.N, device=DEV)
@@ -363,7 +363,7 @@ def _heavy(w, n_rows, seed):
     lens = [int((sel[:, bs:] == j).any(dim=-1).sum()) for j in (0, 1, w.topk - 2)]
     say(f"  {len(rows)} sampled rows; list lengths over (batch, group) of blocks 0, 1, {w.topk - 2}: {lens}")
     ref = O.sparse_bwd(f32(x["q"][bt[:, 0], bt[:, 1]]), f32(x["k"]), f32(x["v"]), f32(x["dO"][bt[:, 0], bt[:, 1]]),
-                       f32(x["q_idx"][bt[:, 0], bt[:, 1]]), f32(x["k_idx"]), s, bs, True, rows=rows, o=f32(o_in))
+                       f32(x["q_idx"][bt[:, 0], bt[:, 1]]), f32(x["k_idx"]), s, bs, causal, rows=rows, o=f32(o_in))
     _check_rows(w, gr, ref, bt)
     # dk, dv per (batch, block, group); dk_idx per (batch, block).  Only
     # slices some sampled row selected can be nonzero: those are compared with
@@ -439,6 +439,20 @@ def test_bwd_g16_heavy_lists():
     w = msa_inputs.Workload("bwd-heavy-g16", B=1, N=16384, H_q=32, H_kv=2, d=128, d_idx=64, topk=16,
                             backward=True, seed=62)
     _heavy(w, 64, 62)
+
+
+def test_bwd_noncausal_sampled():
+    # Every query sees every block; rows only (a block is chosen by most rows
+    # here, which the heavy-list case below covers in full).
+    w = msa_inputs.Workload("bwd-nc-8k", B=1, N=8192, H_q=32, H_kv=8, d=128, d_idx=64, topk=16,
+                            backward=True, seed=63)
+    _sampled(w, "normal", 96, 63, blocks=[], causal=False)
+
+
+def test_bwd_noncausal_heavy_lists():
+    w = msa_inputs.Workload("bwd-nc-heavy", B=2, N=8192, H_q=32, H_kv=8, d=128, d_idx=64, topk=16,
+                            backward=True, seed=64)
+    _heavy(w, 64, 64, causal=False)
 
 
 def test_bwd_dq_and_forward_deterministic():

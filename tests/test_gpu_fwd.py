@@ -115,15 +115,15 @@ def test_bf16_forward_full_multi_tile():
     _check_full(w)
 
 
-def _check_sampled(w, variant, n_rows, seed):
-    x, sel, o, lse = _forward(w, variant)
+def _check_sampled(w, variant, n_rows, seed, causal=True):
+    x, sel, o, lse = _forward(w, variant, causal=causal)
     chunk = fwd_chunk_queries(w)
     seams = [c + dt for c in range(chunk, w.N, chunk) for dt in (-1, 0, 1)]
     rows = sample_rows(w.B, w.N, n_rows, seed, extra=seams)
     bt = torch.tensor(rows, dtype=torch.long)
     q_rows = f32(x["q"][bt[:, 0], bt[:, 1]])
     ref_o, ref_l = O.sparse_fwd(q_rows, f32(x["k"]), f32(x["v"]), sel.cpu().numpy().astype(np.int64),
-                                w.block_size, True, rows=rows)
+                                w.block_size, causal, rows=rows)
     got = f32(o[bt[:, 0], bt[:, 1]])
     got_l = f32(lse[bt[:, 0], bt[:, 1]])
     r, c, dl = max_rel(got, ref_o), cosine(got, ref_o), float(np.abs(got_l - ref_l).max())
@@ -151,6 +151,18 @@ def test_bf16_forward_topk64_sampled():
     # topk 64 over 72 blocks: 64 slots per row to merge (two chunks of loads).
     w = msa_inputs.Workload("bf16-k64", B=1, N=9216, H_q=8, H_kv=2, d=128, d_idx=64, topk=64, seed=98)
     _check_sampled(w, "normal", 96, 98)
+
+
+def test_bf16_forward_d64_sampled():
+    # d = 64, d_idx = 32 with multi-item lists.
+    w = msa_inputs.Workload("bf16-d64-8k", B=2, N=8192, H_q=16, H_kv=4, d=64, d_idx=32, topk=16, seed=97)
+    _check_sampled(w, "normal", 96, 97)
+
+
+def test_bf16_forward_noncausal_sampled():
+    # Every query sees every block (its own block unmasked too).
+    w = msa_inputs.Workload("bf16-nc-8k", B=1, N=8192, H_q=32, H_kv=8, d=128, d_idx=64, topk=16, seed=96)
+    _check_sampled(w, "normal", 128, 96, causal=False)
 
 
 def test_bf16_forward_1m_sampled():
