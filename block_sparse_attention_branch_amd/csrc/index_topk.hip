@@ -65,10 +65,16 @@ __device__ inline void hold_in_registers(const F& x) {
   for (int i = 0; i < (int)(sizeof(F) / 4); ++i) asm volatile("" ::"v"(v.w[i]));
 }
 
-template <typename T, int DIDX, int CAP>
 // A list of 63 entries (topk 64) needs the registers of a whole SIMD: one
-// workgroup per CU then, two otherwise.
-__global__ __launch_bounds__(kIdxThreads, (CAP > 31 ? 1 : 2)) void index_topk_kernel(
+// workgroup per CU then; FP8 with lists of up to 15 (half-block passes) fits
+// three, the others two.
+template <typename T, int CAP>
+constexpr int idx_workgroups_per_cu() {
+  return CAP > 31 ? 1 : ((std::is_same<T, fp8e4m3>::value && CAP <= 15) ? 3 : 2);
+}
+
+template <typename T, int DIDX, int CAP>
+__global__ __launch_bounds__(kIdxThreads, (idx_workgroups_per_cu<T, CAP>())) void index_topk_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, int32_t* __restrict__ block_idx,
     float* __restrict__ pooled, int N, int H_kv, int topk, int causal, int GT, int n_qtiles,
     int n_gtiles) {
@@ -257,11 +263,91 @@ __global__ __launch_bounds__(kIdxThreads, (CAP > 31 ? 1 : 2)) void index_topk_ke
       j_prev = j;
     }
   };
+  // Half-block passes (64 keys, 64 accumulator registers): the products of
+  // row tiles 2h, 2h+1 and their running maximum.  FP8 with lists of up to 15
+  // takes a block in two such passes, which leaves room for three waves per
+  // SIMD (154 VGPRs against 210): 4.2 -> 3.7 ms at N = 128K, 233 -> 214 ms at
+  // 1M.  bf16 keeps the whole-block products: its B operands and staging take
+  // 24 more registers, so the same scheme spilled (8 VGPRs) and ran 2-8%
+  // slower.
+  auto products_half = [&](int buf, int h, f32x16 (&a0)[2], f32x16 (&a1)[2]) __attribute__((always_inline)) {
+    const T* tile = lds + buf * C::TILE_ELEMS;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int mt = 2 * h + m;
+      a0[m] = zero16();
+      a1[m] = zero16();
+      const T* ap = tile + (mt * 32 + (lane & 31)) * C::PITCH + KPL * (lane >> 5);
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        const typename M::frag a = M::load(ap + ks * 2 * KPL);
+        a0[m] = M::mma(a, qf[0][ks], a0[m]);
+        a1[m] = M::mma(a, qf[1][ks], a1[m]);
+      }
+    }
+  };
+  auto pool_half = [&](int j, int h, bool is_own, f32x16 (&a0)[2], f32x16 (&a1)[2], float& run0,
+                       float& run1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int mt = 2 * h + m;
+      if (is_own && causal) {
+        const int t0 = q0 + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int u = j * kBlock + mt * 32 + c_row(v, lane);
+          if (u > t0) a0[m][v] = -INFINITY;
+          if (u > t0 + 32) a1[m][v] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        run0 = fmaxf(run0, a0[m][v]);
+        run1 = fmaxf(run1, a1[m][v]);
+      }
+    }
+  };
+  auto pool_finish = [&](int j, bool is_own, float run0, float run1) __attribute__((always_inline)) {
+    const float recv = swap_half(lane < 32 ? run1 : run0);
+    const float p = fmaxf(lane < 32 ? run0 : run1, recv);   // pooled score of query q0+lane
+    const int tq = q0 + lane;
+    if (pooled != nullptr && tq < N) pooled[(((size_t)b * N + tq) * H_kv + g) * nblk + j] = p;
+    if (!is_own) {
+      p_prev = p;
+      j_prev = j;
+    }
+  };
   // The next block is loaded at the top of each block and goes to the other
   // LDS buffer right after this block's products are issued, so its
   // registers are not held (or re-loaded by the compiler) across the block's
   // vector work.
-  if constexpr (!std::is_same<T, float>::value) {
+  if constexpr (std::is_same<T, fp8e4m3>::value && CAP <= 15) {
+    for (int j = 0; j <= jlast; ++j) {
+      const int buf = j & 1;
+      const bool more = j < jlast;
+      if (more) load_block(j + 1);
+      const bool visible = wave_valid && (!causal || j <= own);
+      const bool is_own = j == own;
+      const bool work = visible && (!is_own || pooled != nullptr);
+      f32x16 a0[2], a1[2];
+      float run0 = -INFINITY, run1 = -INFINITY;
+      if (work) products_half(buf, 0, a0, a1);
+      if (more) store_block(buf ^ 1);
+      if (work) {
+        if (j_prev >= 0) {
+          offer(p_prev, j_prev);
+          j_prev = -1;
+        }
+        pool_half(j, 0, is_own, a0, a1, run0, run1);
+        products_half(buf, 1, a0, a1);
+      }
+      __syncthreads();
+      if (work) {
+        pool_half(j, 1, is_own, a0, a1, run0, run1);
+        pool_finish(j, is_own, run0, run1);
+      }
+    }
+  } else if constexpr (!std::is_same<T, float>::value) {
     // bf16 and FP8: the barrier that completes the next block's tile comes
     // before this block's vector work (measured: FP8 3.6% faster at 1M).
     // bf16 up to topk 16 then reads the next block's row tile 0 right after
